@@ -1,0 +1,181 @@
+/*
+ * mxq.h -- C ABI of libmxq: OCP MXFP4 block quantization and the W4A4 / W4A8 GEMMs that
+ * consume it, with a bf16 reference GEMM and whole-output SQNR, for AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Sources (web pages, cited by title and section):
+ *  [Q13] "AMD Quark adds native W4A8 mixed-precision for Wan2.2 video generation on
+ *        MI350", section "Quark quantization pipeline and mixed-precision selection":
+ *        MXFP4 weights in both modes; dynamic MXFP4 activations for W4A4; static FP8
+ *        E4M3 activations for W4A8; BF16 is the quality ceiling; blocks are scored by
+ *        the SQNR of their whole output against BF16.
+ *  [FLX] "AMD Quark: 1.92x faster FLUX.1-dev with MXFP4 on Instinct MI350", sections
+ *        "MXFP4 quantization for diffusion models" and "What is MXFP4": 4-bit
+ *        elements; 32-element blocks sharing one scale; the GEMM consumes MXFP4 inputs
+ *        directly, with no dequantization phase.
+ *  [MXA] "MXAttention: Data-Free Optimal Scaling and Pre-Normalization Quantization for
+ *        MXFP4 Attention", section "What it actually does": the shared scale is an
+ *        E8M0 power of two with no mantissa.
+ *  [ORK] "Exp 2026-08-22 W4A4 Reference Model", section "Status": a linear per-group
+ *        scale factors out of each group's partial sum and is applied in the fp32 drain.
+ *  Format details the pages leave open follow OCP Microscaling Formats v1.0: E2M1
+ *  elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 and negatives), E8M0 bias 127, OCP FP8
+ *  E4M3 (max 448).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are DEVICE pointers (HBM) owned by the caller; the library never
+ *    allocates, frees or retains them.  Scalars are passed by value.  The one
+ *    host-visible result (mxq_sqnr's three doubles) is written to device memory.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues
+ *    work on it and returns; nothing synchronizes.  Device-side faults surface at the
+ *    caller's next synchronization.
+ *  - Return value: MXQ_OK, or an error code with a message available from
+ *    mxq_last_error() on the same thread.  Arguments are validated before anything is
+ *    launched: an error return means nothing was enqueued.  MXQ_ERR_HIP reports a HIP
+ *    launch error (e.g. no device present).
+ *  - Empty problems (rows == 0, M == 0 or N == 0) are valid and enqueue nothing.
+ *  - Layouts (all row-major):
+ *      MXFP4 codes  : uint8 [rows x ld_codes], byte j of a row holds element 2j in the
+ *                     low nibble and element 2j+1 in the high nibble; an E2M1 code is
+ *                     sign<<3 | exponent(2 bits, bias 1)<<1 | mantissa(1 bit).
+ *      MXFP4 scales : uint8 [rows x ld_scales], one E8M0 byte per 32-element block
+ *                     along the row; value 2^(byte - 127).
+ *      FP8          : uint8 [rows x ld], OCP E4M3.
+ *      bf16         : uint16 bit patterns.
+ *    The quantizer's output is exactly the GEMMs' input: there is no hidden reshuffle.
+ *    GEMM weights W are N x K with K contiguous (nn.Linear layout); out = A * W^T.
+ *  - Thread safety: no global mutable state except the thread-local error message.
+ */
+#ifndef MXQ_H
+#define MXQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MXQ_ABI_VERSION 1
+
+typedef enum {
+  MXQ_OK = 0,
+  MXQ_ERR_INVALID_ARG = 1, /* bad size, pointer, alignment or leading dimension */
+  MXQ_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve (e.g. unknown dtype) */
+  MXQ_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+} mxq_status;
+
+typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1 } mxq_dtype;
+
+/*
+ * mxq_quantize -- MXFP4 block quantization along each row ([FLX] "What is MXFP4";
+ * [MXA] "What it actually does"; [Q13] dynamic activations).
+ * For each row and each block of 32 consecutive elements starting at a multiple of 32:
+ *   amax = max |x|;  scale byte s = max(E(amax) - 2, 0), E = biased binary32 exponent
+ *   field, i.e. X = 2^(clamp(floor(log2 amax) - 2, -127, 127)), all-zero block -> 0x00;
+ *   code = E2M1 round-to-nearest-even of x / X, saturated to +-6, sign bit from x.
+ * x      : `rows` rows of `cols` elements of type `dt`, row pitch `ld_x` elements.
+ *          Base and row pitch in bytes must be multiples of 16.  Finite values only.
+ * codes  : out, rows x cols/2 bytes, pitch ld_codes bytes (multiple of 16, base 16-aligned).
+ * scales : out, rows x cols/32 bytes, pitch ld_scales bytes (any alignment).
+ * Errors : cols % 32 != 0, negative sizes, pitches below the row width, NULL pointers,
+ *          misalignment -> MXQ_ERR_INVALID_ARG; unknown dt -> MXQ_ERR_UNSUPPORTED.
+ */
+mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                        uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                        void* stream);
+
+/*
+ * mxq_quantize_fp8 -- static FP8 E4M3 activation quantization for W4A8 ([Q13]).
+ *   q = E4M3(fl32(x * inv_scale)): one binary32 multiply (round to nearest even), then
+ *   E4M3 round-to-nearest-even saturating at +-448 (never NaN); sign bit from the product.
+ * inv_scale is the static per-tensor multiplier, normally fl32(448 / amax) with amax
+ * measured once ahead of time (mxq_absmax); the GEMM takes s_a = fl32(amax / 448).
+ * x : rows x cols of `dt`, pitch ld_x elements; base and pitch 16-byte aligned.
+ * q : out, rows x cols bytes, pitch ld_q bytes; base and pitch multiples of 16.
+ * cols must be a multiple of 16.  Errors as for mxq_quantize; inv_scale must be finite
+ * and > 0.
+ */
+mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                            float inv_scale, uint8_t* q, int64_t ld_q, void* stream);
+
+/*
+ * mxq_absmax -- max |x| over a rows x cols tensor, written as one float to *out (device).
+ * The calibration step that fixes the static FP8 scale; not part of a W4A8 call.
+ * Same layout and alignment rules as mxq_quantize_fp8 (cols % 8 == 0).
+ */
+mxq_status mxq_absmax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                      float* out, void* stream);
+
+/*
+ * mxq_gemm_w4a4 -- out = bf16_RNE( sum_b 2^(SA[m,b] + SW[n,b] - 254) *
+ *                  sum_{i<32} e2m1(QA[m,32b+i]) * e2m1(QW[n,32b+i]) ), fp32 accumulation
+ * ([Q13] W4A4; [FLX] MXFP4 consumed directly; [ORK] scales applied to block partials).
+ * a_codes  : M x K/2 bytes, contiguous rows; a_scales: M x K/32 bytes, contiguous rows.
+ * w_codes  : N x K/2 bytes, contiguous rows; w_scales: N x K/32 bytes, contiguous rows.
+ * out_bf16 : M x N bf16, row pitch ld_out elements (>= N).
+ * K % 32 == 0 (K == 0 writes zeros).  Code bases must be 16-byte aligned.
+ */
+mxq_status mxq_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         int64_t M, int64_t N, int64_t K, uint16_t* out_bf16, int64_t ld_out,
+                         void* stream);
+
+/*
+ * mxq_gemm_w4a8 -- out = bf16_RNE( fl32( a_scale * sum_b 2^(SW[n,b] - 127) *
+ *                  sum_{i<32} e4m3(QA8[m,32b+i]) * e2m1(QW[n,32b+i]) ) ) ([Q13] W4A8).
+ * a_fp8   : M x K bytes (E4M3), contiguous rows, base 16-byte aligned.
+ * a_scale : the static dequantization scale s_a (finite).
+ * W, out and K as for mxq_gemm_w4a4.
+ */
+mxq_status mxq_gemm_w4a8(const uint8_t* a_fp8, float a_scale,
+                         const uint8_t* w_codes, const uint8_t* w_scales,
+                         int64_t M, int64_t N, int64_t K, uint16_t* out_bf16, int64_t ld_out,
+                         void* stream);
+
+/*
+ * mxq_gemm_bf16 -- bf16 reference for SQNR ([Q13] BF16 quality ceiling):
+ * out = bf16_RNE(sum_k a[m,k] * w[n,k]), fp32 accumulation, over unquantized operands.
+ * a : M x K bf16, contiguous rows; w : N x K bf16, contiguous rows; bases 16-byte
+ * aligned; K % 32 == 0.  out as for mxq_gemm_w4a4.
+ */
+mxq_status mxq_gemm_bf16(const uint16_t* a, const uint16_t* w, int64_t M, int64_t N, int64_t K,
+                         uint16_t* out, int64_t ld_out, void* stream);
+
+/*
+ * mxq_sqnr -- whole-output SQNR of `test` against `ref` ([Q13] block-output SQNR):
+ *   S = sum ref^2, N = sum (ref - test)^2 over all rows x cols bf16 elements (exactly
+ *   widened), dB = 10 log10(S / N); N == 0 -> +inf, S == N == 0 -> NaN.
+ * Deterministic: fixed partition, per-thread fp32 -> per-workgroup fp64 -> one final
+ * fp64 pass.  workspace: device scratch of at least mxq_sqnr_workspace_bytes(rows*cols)
+ * bytes (8-byte aligned), owned by the caller.  out3: device double[3] = {S, N, dB}.
+ * ref/test pitches in elements; bases 16-byte aligned, pitches multiples of 8, cols % 8 == 0.
+ */
+size_t mxq_sqnr_workspace_bytes(int64_t n_elements);
+mxq_status mxq_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols,
+                    int64_t ld_ref, int64_t ld_test, void* workspace, size_t ws_bytes,
+                    double* out3, void* stream);
+
+/*
+ * mxq_dequantize -- MXFP4 -> bf16: y = bf16(e2m1(code) * 2^(scale - 127)) (rounded to
+ * nearest even only where the product leaves bf16's range: below 2^-133 or above 2^127).
+ * The quantize-dequantize (QDQ) emulation step ([Q13]: W4A8 quality was measured by
+ * QDQ emulation).  codes/scales as produced by mxq_quantize; y: rows x cols bf16, pitch
+ * ld_y elements, base and pitch 16-byte aligned.
+ */
+mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                          int64_t ld_scales, int64_t rows, int64_t cols, uint16_t* y,
+                          int64_t ld_y, void* stream);
+
+/* Thread-local message for the last failing call on this thread ("" if none). Valid
+ * until the next mxq_* call on the same thread. */
+const char* mxq_last_error(void);
+
+/* MXQ_ABI_VERSION of the loaded library. */
+int mxq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXQ_H */

@@ -1,0 +1,356 @@
+// Block-scaled MFMA GEMMs for gfx950: W4A4 (MXFP4 x MXFP4), W4A8 (MXFP4 weights x FP8
+// E4M3 activations) and the bf16 reference, all out = A * W^T with fp32 accumulation and
+// a bf16 (round to nearest even) epilogue.
+//
+// What is computed ("AMD Quark adds native W4A8 mixed-precision for Wan2.2 ...", section
+// "Quark quantization pipeline and mixed-precision selection"; "AMD Quark: 1.92x faster
+// FLUX.1-dev ...", section "MXFP4 quantization for diffusion models": the GEMM consumes
+// MXFP4 directly with no dequantization phase; "Exp 2026-08-22 W4A4 Reference Model",
+// section "Status": a linear per-group scale factors out of the group's partial sum):
+//   W4A4: out[m,n] = sum_b 2^(SA[m,b]+SW[n,b]-254) * sum_i e2m1(QA[m,32b+i]) e2m1(QW[n,32b+i])
+//   W4A8: out[m,n] = s_a * sum_b 2^(SW[n,b]-127) * sum_i e4m3(QA8[m,32b+i]) e2m1(QW[n,32b+i])
+// The per-block scales are applied inside v_mfma_scale_f32_32x32x64_f8f6f4, which takes
+// one E8M0 byte per (row, 32-K block) per operand, so no value is ever dequantized.
+//
+// Tiling (one workgroup = 4 waves = a 256 (m) x 256 (n) output tile; one wave = 128 x 128):
+//  * The weight tile is the MFMA A operand and the activation tile the B operand, so
+//    every lane finishes holding 4 consecutive output columns of one row (8-byte stores).
+//  * K advances in windows of 128 bytes per row (256 fp4 / 128 fp8 / 64 bf16 values).
+//    Each window is staged global -> registers -> LDS, double buffered (2 x 64 KB), with
+//    16-byte chunks XOR-swizzled by row so MFMA fragment reads are bank-conflict free.
+//  * Inside a window the MFMA K-slots are assigned so that lane group g (lanes 32g..32g+31)
+//    at MFMA step t holds K-block 4g+t (fp4): a lane reads contiguous 16-byte chunks and
+//    one 32-bit word holds its four scale bytes, selected by op_sel = t.  Any assignment
+//    is valid as long as both operands and the scales agree; the sum over K is the same.
+//  * FP8 operands occupy the MFMA K range in two halves (per lane: 16 bytes from the low
+//    half, 16 from the high half), so W4A8 reads two 16-byte chunks per fragment.
+//  * Workgroups are renumbered so that each XCD (dispatched round-robin) walks a
+//    contiguous run of tiles, grouped 4 m-tiles wide, keeping panels shared in its L2.
+//  * Ragged M/N/K tails are zero-filled by buffer-load range checks and masked stores.
+#include "mxq_device.hpp"
+#include "mxq_internal.hpp"
+
+namespace mxq {
+namespace {
+
+constexpr int BM = 256;   // activation rows per workgroup
+constexpr int BN = 256;   // weight rows per workgroup
+constexpr int NT = 256;   // threads per workgroup
+constexpr int GROUP_M = 4;
+
+template <int MODE> struct Cfg;
+template <> struct Cfg<GEMM_W4A4> {
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256;
+};
+template <> struct Cfg<GEMM_W4A8> {
+  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128;
+};
+template <> struct Cfg<GEMM_BF16> {
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64;
+};
+
+struct Params {
+  const uint8_t* a;
+  const uint8_t* a_scales;
+  const uint8_t* w;
+  const uint8_t* w_scales;
+  uint16_t* out;
+  int64_t ld_out;
+  int M, N;
+  uint32_t a_row_bytes, w_row_bytes, scale_row_bytes;
+  int nwin, tiles_m, tiles_n;
+  float a_scale;
+  int vec_store;
+  int scale_dword_ok;
+};
+
+__device__ __forceinline__ uint32_t swz128(uint32_t row, uint32_t chunk) {
+  return row * 128u + ((chunk ^ (row & 7u)) << 4);
+}
+__device__ __forceinline__ uint32_t swz64(uint32_t row, uint32_t chunk) {
+  return row * 64u + ((chunk ^ ((row >> 1) & 3u)) << 4);
+}
+
+__device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
+__device__ __forceinline__ v8i cat(v4i x, v4i y) { return v8i{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]}; }
+
+// Four scale bytes of one row starting at byte `col`; bytes past the row read as 0
+// (a finite 2^-127 multiplying zero-filled data).
+__device__ __forceinline__ uint32_t load_scale4(__amdgpu_buffer_rsrc_t r, uint32_t row_off, uint32_t col,
+                                                uint32_t row_bytes, int dword_ok) {
+  if (dword_ok) {
+    const uint32_t off = (col + 4u <= row_bytes) ? row_off + col : 0x80000000u;
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+  }
+  uint32_t v = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint32_t off = (col + b < row_bytes) ? row_off + col + b : 0x80000000u;
+    v |= ((uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, off, 0, 0) & 0xFFu) << (8 * b);
+  }
+  return v;
+}
+
+template <int MODE, int T>
+__device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const uint8_t* lds_a, const uint8_t* lds_w,
+                                          uint32_t wm, uint32_t wn, uint32_t lane, const uint32_t (&scw)[4],
+                                          const uint32_t (&sca)[4]) {
+  const uint32_t g = lane >> 5, r32 = lane & 31;
+  if constexpr (MODE == GEMM_W4A4) {
+    v4i wf[4], af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wf[i] = *reinterpret_cast<const v4i*>(lds_w + swz128(wn * 128 + 32 * i + r32, 4 * g + T));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      af[j] = *reinterpret_cast<const v4i*>(lds_a + swz128(wm * 128 + 32 * j + r32, 4 * g + T));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(wf[i]), widen(af[j]), acc[i][j], 4, 4, T,
+                                                                    (int)scw[i], T, (int)sca[j]);
+  } else if constexpr (MODE == GEMM_W4A8) {
+    v4i wf[4], alo[4], ahi[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wf[i] = *reinterpret_cast<const v4i*>(lds_w + swz64(wn * 128 + 32 * i + r32, 2 * g + T));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = wm * 128 + 32 * j + r32;
+      alo[j] = *reinterpret_cast<const v4i*>(lds_a + swz128(row, 2 * T + g));
+      ahi[j] = *reinterpret_cast<const v4i*>(lds_a + swz128(row, 4 + 2 * T + g));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(wf[i]), cat(alo[j], ahi[j]), acc[i][j], 4,
+                                                                    0, T, (int)scw[i], 0, 127);
+  } else {
+    v4i wf[4], af[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      wf[i] = *reinterpret_cast<const v4i*>(lds_w + swz128(wn * 128 + 32 * i + r32, 4 * g + T));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      af[j] = *reinterpret_cast<const v4i*>(lds_a + swz128(wm * 128 + 32 * j + r32, 4 * g + T));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, wf[i]),
+                                                            __builtin_bit_cast(bf16x8, af[j]), acc[i][j], 0, 0, 0);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p) {
+  using C = Cfg<MODE>;
+  constexpr uint32_t A_TILE = BM * C::A_RB;
+  constexpr uint32_t W_TILE = BN * C::W_RB;
+  constexpr uint32_t BUF = A_TILE + W_TILE;
+  constexpr int A_CH = A_TILE / 16 / NT;   // 16-byte chunks per thread per window
+  constexpr int W_CH = W_TILE / 16 / NT;
+  constexpr int A_CPR = C::A_RB / 16;      // chunks per row
+  constexpr int W_CPR = C::W_RB / 16;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * BUF];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t wm = wave & 1, wn = wave >> 1;
+
+  // ---- tile order: contiguous run per XCD, grouped GROUP_M m-tiles wide ----
+  const int nt = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q8 = nt >> 3, r8 = nt & 7;
+  const int seq = xcd * q8 + min(xcd, r8) + local;
+  const int group = seq / (GROUP_M * p.tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(GROUP_M, p.tiles_m - first_m);
+  const int in_group = seq - group * GROUP_M * p.tiles_n;
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  if (p.nwin > 0) {
+    // per-thread staging geometry (fixed across windows)
+    const uint32_t a_c = tid % A_CPR, a_r = tid / A_CPR;
+    const uint32_t w_c = tid % W_CPR, w_r = tid / W_CPR;
+    constexpr uint32_t A_RSTEP = NT / A_CPR, W_RSTEP = NT / W_CPR;
+
+    // scale planes (unused by the bf16 reference: zero-length resources)
+    const bool has_ws = MODE != GEMM_BF16, has_as = MODE == GEMM_W4A4;
+    const __amdgpu_buffer_rsrc_t rsw =
+        make_rsrc(has_ws ? p.w_scales + (int64_t)n0 * p.scale_row_bytes : p.w, has_ws ? rows_w * p.scale_row_bytes : 0);
+    const __amdgpu_buffer_rsrc_t rsa =
+        make_rsrc(has_as ? p.a_scales + (int64_t)m0 * p.scale_row_bytes : p.a, has_as ? rows_a * p.scale_row_bytes : 0);
+    uint32_t sa_off[4], sw_off[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sw_off[i] = (wn * 128 + 32 * i + (lane & 31)) * p.scale_row_bytes;
+      sa_off[i] = (wm * 128 + 32 * i + (lane & 31)) * p.scale_row_bytes;
+    }
+
+    v4i sta[A_CH], stw[W_CH];
+    uint32_t scw[4] = {0, 0, 0, 0}, sca[4] = {0, 0, 0, 0}, scw_n[4] = {0, 0, 0, 0}, sca_n[4] = {0, 0, 0, 0};
+
+    auto load_window = [&](int w) {
+      const uint32_t abase = (uint32_t)w * C::A_RB + a_c * 16;
+      const bool a_in = abase + 16 <= p.a_row_bytes;
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) {
+        const uint32_t off = a_in ? (a_r + i * A_RSTEP) * p.a_row_bytes + abase : 0x80000000u;
+        sta[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, off, 0, 0);
+      }
+      const uint32_t wbase = (uint32_t)w * C::W_RB + w_c * 16;
+      const bool w_in = wbase + 16 <= p.w_row_bytes;
+#pragma unroll
+      for (int i = 0; i < W_CH; ++i) {
+        const uint32_t off = w_in ? (w_r + i * W_RSTEP) * p.w_row_bytes + wbase : 0x80000000u;
+        stw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
+      }
+      if constexpr (MODE == GEMM_W4A4) {
+        const uint32_t col = (uint32_t)w * 8 + 4 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) scw_n[i] = load_scale4(rsw, sw_off[i], col, p.scale_row_bytes, p.scale_dword_ok);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sca_n[j] = load_scale4(rsa, sa_off[j], col, p.scale_row_bytes, p.scale_dword_ok);
+      } else if constexpr (MODE == GEMM_W4A8) {
+        const uint32_t col = (uint32_t)w * 4;
+        const uint32_t sh = 16 * (lane >> 5);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          scw_n[i] = load_scale4(rsw, sw_off[i], col, p.scale_row_bytes, p.scale_dword_ok) >> sh;
+      }
+    };
+    auto store_window = [&](uint32_t buf) {
+      uint8_t* la = lds + buf;
+      uint8_t* lw = lds + buf + A_TILE;
+#pragma unroll
+      for (int i = 0; i < A_CH; ++i) *reinterpret_cast<v4i*>(la + swz128(a_r + i * A_RSTEP, a_c)) = sta[i];
+#pragma unroll
+      for (int i = 0; i < W_CH; ++i) {
+        if constexpr (C::W_RB == 128)
+          *reinterpret_cast<v4i*>(lw + swz128(w_r + i * W_RSTEP, w_c)) = stw[i];
+        else
+          *reinterpret_cast<v4i*>(lw + swz64(w_r + i * W_RSTEP, w_c)) = stw[i];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        scw[i] = scw_n[i];
+        sca[i] = sca_n[i];
+      }
+    };
+
+    load_window(0);
+    store_window(0);
+    __syncthreads();
+    if (p.nwin > 1) load_window(1);
+
+    for (int w = 0; w < p.nwin; ++w) {
+      const uint8_t* la = lds + (w & 1) * BUF;
+      const uint8_t* lw = la + A_TILE;
+      mfma_step<MODE, 0>(acc, la, lw, wm, wn, lane, scw, sca);
+      mfma_step<MODE, 1>(acc, la, lw, wm, wn, lane, scw, sca);
+      if constexpr (C::STEPS == 4) {
+        mfma_step<MODE, 2>(acc, la, lw, wm, wn, lane, scw, sca);
+        mfma_step<MODE, 3>(acc, la, lw, wm, wn, lane, scw, sca);
+      }
+      if (w + 1 < p.nwin) {
+        store_window(((w + 1) & 1) * BUF);
+        if (w + 2 < p.nwin) load_window(w + 2);
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: fp32 -> bf16 (RNE), lane owns 4 consecutive columns per store ----
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + (int)(wm * 128 + 32 * j + r32);
+    if (m >= p.M) continue;
+    uint16_t* orow = p.out + (int64_t)m * p.ld_out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
+        float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+        float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+        if constexpr (MODE == GEMM_W4A8) {
+          v0 *= p.a_scale;
+          v1 *= p.a_scale;
+          v2 *= p.a_scale;
+          v3 *= p.a_scale;
+        }
+        const unsigned lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
+        if (p.vec_store && n + 4 <= p.N) {
+          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+        } else {
+          const uint16_t h[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi, (uint16_t)(hi >> 16)};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < p.N) orow[n + e] = h[e];
+        }
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,
+                       const uint8_t* w_scales, float a_scale, int64_t M, int64_t N, int64_t K,
+                       uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  Params p;
+  p.a = static_cast<const uint8_t*>(a);
+  p.a_scales = a_scales;
+  p.w = static_cast<const uint8_t*>(w);
+  p.w_scales = w_scales;
+  p.out = out;
+  p.ld_out = ld_out;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.scale_row_bytes = (uint32_t)(K / 32);
+  p.scale_dword_ok = (K / 32) % 4 == 0 ? 1 : 0;
+  p.a_scale = a_scale;
+  p.vec_store = (ld_out % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0) ? 1 : 0;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(NT);
+  switch (mode) {
+    case GEMM_W4A4:
+      p.a_row_bytes = p.w_row_bytes = (uint32_t)(K / 2);
+      p.nwin = (int)((K + Cfg<GEMM_W4A4>::K_WIN - 1) / Cfg<GEMM_W4A4>::K_WIN);
+      hipLaunchKernelGGL(gemm_kernel<GEMM_W4A4>, grid, block, 0, stream, p);
+      break;
+    case GEMM_W4A8:
+      p.a_row_bytes = (uint32_t)K;
+      p.w_row_bytes = (uint32_t)(K / 2);
+      p.nwin = (int)((K + Cfg<GEMM_W4A8>::K_WIN - 1) / Cfg<GEMM_W4A8>::K_WIN);
+      hipLaunchKernelGGL(gemm_kernel<GEMM_W4A8>, grid, block, 0, stream, p);
+      break;
+    case GEMM_BF16:
+      p.a_row_bytes = p.w_row_bytes = (uint32_t)(K * 2);
+      p.nwin = (int)((K + Cfg<GEMM_BF16>::K_WIN - 1) / Cfg<GEMM_BF16>::K_WIN);
+      hipLaunchKernelGGL(gemm_kernel<GEMM_BF16>, grid, block, 0, stream, p);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace mxq

@@ -1,0 +1,230 @@
+// C ABI of libmxq: argument validation, error reporting and dispatch to the gfx950
+// launchers.  Every check runs before anything is enqueued, so an error return means the
+// stream was not touched.  The only mutable state is the thread-local error message.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/mxq.h"
+#include "mxq_internal.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+mxq_status fail(mxq_status code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+mxq_status ok() {
+  g_error.clear();
+  return MXQ_OK;
+}
+
+mxq_status hip_status(const char* fn, hipError_t e) {
+  if (e != hipSuccess) return fail(MXQ_ERR_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int dtype_bytes(mxq_dtype dt) {
+  switch (dt) {
+    case MXQ_F32: return 4;
+    case MXQ_BF16: return 2;
+  }
+  return 0;
+}
+
+// Shared checks for a rows x cols input of dtype dt with pitch ld (elements).
+mxq_status check_input(const char* fn, const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld,
+                       int64_t col_multiple) {
+  if (dtype_bytes(dt) == 0) return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dt);
+  if (rows < 0 || cols < 0) return fail(MXQ_ERR_INVALID_ARG, "%s: negative size (%lld x %lld)", fn, (long long)rows, (long long)cols);
+  if (cols % col_multiple != 0)
+    return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of %lld", fn, (long long)cols,
+                (long long)col_multiple);
+  if (ld < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_x (%lld) < cols (%lld)", fn, (long long)ld, (long long)cols);
+  if (rows > 0 && cols > 0) {
+    if (!x) return fail(MXQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
+    if (!aligned(x, 16) || (ld * dtype_bytes(dt)) % 16 != 0)
+      return fail(MXQ_ERR_INVALID_ARG, "%s: x base and row pitch must be 16-byte aligned", fn);
+  }
+  if (rows > (int64_t)0x7FFFFFFF || cols > (int64_t)0x7FFFFFFF)
+    return fail(MXQ_ERR_INVALID_ARG, "%s: dimension exceeds 2^31-1", fn);
+  if ((rows * (cols / 8 > 0 ? cols / 8 : 1)) >= ((int64_t)1 << 32))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large (more than 2^35 elements)", fn);
+  return MXQ_OK;
+}
+
+mxq_status check_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const void* out, int64_t ld_out) {
+  if (M < 0 || N < 0 || K < 0)
+    return fail(MXQ_ERR_INVALID_ARG, "%s: negative size (M=%lld N=%lld K=%lld)", fn, (long long)M, (long long)N,
+                (long long)K);
+  if (K % 32 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: K (%lld) must be a multiple of 32", fn, (long long)K);
+  if (M > (int64_t)0x7FFFFFFF - 256 || N > (int64_t)0x7FFFFFFF - 256 || K > ((int64_t)1 << 21))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: dimension too large", fn);
+  if (ld_out < N) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_out (%lld) < N (%lld)", fn, (long long)ld_out, (long long)N);
+  if (M > 0 && N > 0) {
+    if (!out) return fail(MXQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
+    if (!aligned(out, 2)) return fail(MXQ_ERR_INVALID_ARG, "%s: out must be 2-byte aligned", fn);
+    const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+    if (tiles > 0x7FFFFFFF) return fail(MXQ_ERR_INVALID_ARG, "%s: problem too large", fn);
+  }
+  return MXQ_OK;
+}
+
+mxq_status check_operand(const char* fn, const char* name, const void* p, int64_t rows, int64_t K, int align) {
+  if (rows > 0 && K > 0) {
+    if (!p) return fail(MXQ_ERR_INVALID_ARG, "%s: %s is NULL", fn, name);
+    if (!aligned(p, (uintptr_t)align)) return fail(MXQ_ERR_INVALID_ARG, "%s: %s must be %d-byte aligned", fn, name, align);
+  }
+  return MXQ_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
+
+const char* mxq_last_error(void) { return g_error.c_str(); }
+
+mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                        int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
+  const char* fn = "mxq_quantize";
+  mxq_status st = check_input(fn, x, dt, rows, cols, ld_x, 32);
+  if (st != MXQ_OK) return st;
+  if (ld_codes < cols / 2) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_codes (%lld) < cols/2", fn, (long long)ld_codes);
+  if (ld_scales < cols / 32) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_scales (%lld) < cols/32", fn, (long long)ld_scales);
+  if (rows > 0 && cols > 0) {
+    if (!codes || !scales) return fail(MXQ_ERR_INVALID_ARG, "%s: codes/scales is NULL", fn);
+    if (!aligned(codes, 16) || ld_codes % 16 != 0)
+      return fail(MXQ_ERR_INVALID_ARG, "%s: codes base and ld_codes must be multiples of 16 bytes", fn);
+  }
+  return hip_status(fn, mxq::launch_quantize_mxfp4(x, dt == MXQ_F32, rows, cols, ld_x, codes, ld_codes, scales,
+                                                   ld_scales, as_stream(stream)));
+}
+
+mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, float inv_scale,
+                            uint8_t* q, int64_t ld_q, void* stream) {
+  const char* fn = "mxq_quantize_fp8";
+  mxq_status st = check_input(fn, x, dt, rows, cols, ld_x, 16);
+  if (st != MXQ_OK) return st;
+  if (!(inv_scale > 0.0f) || !(inv_scale < __builtin_inff()))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: inv_scale must be finite and > 0", fn);
+  if (ld_q < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_q (%lld) < cols", fn, (long long)ld_q);
+  if (rows > 0 && cols > 0) {
+    if (!q) return fail(MXQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
+    if (!aligned(q, 16) || ld_q % 16 != 0)
+      return fail(MXQ_ERR_INVALID_ARG, "%s: q base and ld_q must be multiples of 16 bytes", fn);
+  }
+  return hip_status(fn, mxq::launch_quantize_fp8(x, dt == MXQ_F32, rows, cols, ld_x, inv_scale, q, ld_q,
+                                                 as_stream(stream)));
+}
+
+mxq_status mxq_absmax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, float* out,
+                      void* stream) {
+  const char* fn = "mxq_absmax";
+  mxq_status st = check_input(fn, x, dt, rows, cols, ld_x, 8);
+  if (st != MXQ_OK) return st;
+  if (!out || !aligned(out, 4)) return fail(MXQ_ERR_INVALID_ARG, "%s: out must be a non-NULL 4-byte aligned pointer", fn);
+  return hip_status(fn, mxq::launch_absmax(x, dt == MXQ_F32, rows, cols, ld_x, out, as_stream(stream)));
+}
+
+mxq_status mxq_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* w_codes,
+                         const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, uint16_t* out_bf16,
+                         int64_t ld_out, void* stream) {
+  const char* fn = "mxq_gemm_w4a4";
+  mxq_status st = check_gemm(fn, M, N, K, out_bf16, ld_out);
+  if (st != MXQ_OK) return st;
+  if (M > 0 && N > 0) {
+    if ((st = check_operand(fn, "a_codes", a_codes, M, K, 16)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "a_scales", a_scales, M, K, 1)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "w_codes", w_codes, N, K, 16)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "w_scales", w_scales, N, K, 1)) != MXQ_OK) return st;
+  }
+  return hip_status(fn, mxq::launch_gemm(mxq::GEMM_W4A4, a_codes, a_scales, w_codes, w_scales, 1.0f, M, N, K,
+                                         out_bf16, ld_out, as_stream(stream)));
+}
+
+mxq_status mxq_gemm_w4a8(const uint8_t* a_fp8, float a_scale, const uint8_t* w_codes, const uint8_t* w_scales,
+                         int64_t M, int64_t N, int64_t K, uint16_t* out_bf16, int64_t ld_out, void* stream) {
+  const char* fn = "mxq_gemm_w4a8";
+  mxq_status st = check_gemm(fn, M, N, K, out_bf16, ld_out);
+  if (st != MXQ_OK) return st;
+  if (!(a_scale == a_scale) || a_scale == __builtin_inff() || a_scale == -__builtin_inff())
+    return fail(MXQ_ERR_INVALID_ARG, "%s: a_scale must be finite", fn);
+  if (M > 0 && N > 0) {
+    if ((st = check_operand(fn, "a_fp8", a_fp8, M, K, 16)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "w_codes", w_codes, N, K, 16)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "w_scales", w_scales, N, K, 1)) != MXQ_OK) return st;
+  }
+  return hip_status(fn, mxq::launch_gemm(mxq::GEMM_W4A8, a_fp8, nullptr, w_codes, w_scales, a_scale, M, N, K,
+                                         out_bf16, ld_out, as_stream(stream)));
+}
+
+mxq_status mxq_gemm_bf16(const uint16_t* a, const uint16_t* w, int64_t M, int64_t N, int64_t K, uint16_t* out,
+                         int64_t ld_out, void* stream) {
+  const char* fn = "mxq_gemm_bf16";
+  mxq_status st = check_gemm(fn, M, N, K, out, ld_out);
+  if (st != MXQ_OK) return st;
+  if (M > 0 && N > 0) {
+    if ((st = check_operand(fn, "a", a, M, K, 16)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "w", w, N, K, 16)) != MXQ_OK) return st;
+  }
+  return hip_status(fn, mxq::launch_gemm(mxq::GEMM_BF16, a, nullptr, w, nullptr, 1.0f, M, N, K, out, ld_out,
+                                         as_stream(stream)));
+}
+
+size_t mxq_sqnr_workspace_bytes(int64_t n_elements) { return mxq::sqnr_workspace_bytes(n_elements); }
+
+mxq_status mxq_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols, int64_t ld_ref,
+                    int64_t ld_test, void* workspace, size_t ws_bytes, double* out3, void* stream) {
+  const char* fn = "mxq_sqnr";
+  if (rows < 0 || cols < 0) return fail(MXQ_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (cols % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
+  if (ld_ref < cols || ld_test < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below cols", fn);
+  if (ld_ref % 8 != 0 || ld_test % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: pitches must be multiples of 8", fn);
+  if (rows > (int64_t)0x7FFFFFFF || cols > (int64_t)0x7FFFFFFF || rows * (cols / 8) >= ((int64_t)1 << 32))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  if (!out3 || !aligned(out3, 8)) return fail(MXQ_ERR_INVALID_ARG, "%s: out3 must be a non-NULL 8-byte aligned pointer", fn);
+  if (!workspace || !aligned(workspace, 8) || ws_bytes < mxq::sqnr_workspace_bytes(rows * cols))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: workspace missing, misaligned or smaller than %zu bytes", fn,
+                mxq::sqnr_workspace_bytes(rows * cols));
+  if (rows > 0 && cols > 0) {
+    if (!ref || !test) return fail(MXQ_ERR_INVALID_ARG, "%s: ref/test is NULL", fn);
+    if (!aligned(ref, 16) || !aligned(test, 16)) return fail(MXQ_ERR_INVALID_ARG, "%s: ref/test must be 16-byte aligned", fn);
+  }
+  return hip_status(fn, mxq::launch_sqnr(ref, test, rows, cols, ld_ref, ld_test, workspace, out3, as_stream(stream)));
+}
+
+mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales,
+                          int64_t rows, int64_t cols, uint16_t* y, int64_t ld_y, void* stream) {
+  const char* fn = "mxq_dequantize";
+  if (rows < 0 || cols < 0) return fail(MXQ_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (cols % 32 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 32", fn, (long long)cols);
+  if (ld_codes < cols / 2 || ld_scales < cols / 32 || ld_y < cols)
+    return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below the row width", fn);
+  if (rows > (int64_t)0x7FFFFFFF || rows * (cols / 32) >= ((int64_t)1 << 30))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  if (rows > 0 && cols > 0) {
+    if (!codes || !scales || !y) return fail(MXQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(codes, 4) || ld_codes % 4 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: codes must be 4-byte aligned", fn);
+    if (!aligned(y, 16) || ld_y % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: y base and pitch must be 16-byte aligned", fn);
+  }
+  return hip_status(fn, mxq::launch_dequantize(codes, ld_codes, scales, ld_scales, rows, cols, y, ld_y,
+                                               as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,330 @@
+// Bandwidth-bound element kernels for gfx950: MXFP4 block quantization, static FP8 E4M3
+// quantization, absolute maximum (static-scale calibration) and MXFP4 dequantization.
+//
+// MXFP4 rule ("AMD Quark: 1.92x faster FLUX.1-dev with MXFP4 on Instinct MI350", section
+// "What is MXFP4": 32-element blocks share one scale; "MXAttention ...", section "What it
+// actually does": the scale is an E8M0 power of two): per block, the scale byte is
+// s = max(E(amax) - 2, 0) with E the biased exponent field of amax, i.e.
+// X = 2^(floor(log2 amax) - 2) clamped at 2^-127, and every element becomes the E2M1
+// value nearest to x / X (ties to even, saturating at +-6).
+//
+// Mapping: four consecutive lanes own one 32-element block (8 elements, 16 bytes of
+// bf16, per lane), so each wave load instruction moves 1 KB of contiguous input and the
+// block maximum is a 2-step DPP reduction inside the quad.  The E2M1 rounding is the
+// gfx950 conversion v_cvt_scalef32_pk_fp4_f32, which computes round-to-nearest-even of
+// x / scale with saturation for power-of-two scales (including the subnormal 2^-127), two
+// elements per instruction (bf16 inputs are widened exactly first).
+#include "mxq_device.hpp"
+#include "mxq_internal.hpp"
+
+namespace mxq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;            // blocks in flight per quad
+constexpr int kBlocksPerIter = kThreads / 4 * kUnroll;
+
+__device__ __forceinline__ float lo_f32(int pair) { return __uint_as_float((unsigned)pair << 16); }
+__device__ __forceinline__ float hi_f32(int pair) { return __uint_as_float((unsigned)pair & 0xFFFF0000u); }
+
+__device__ __forceinline__ unsigned scale_byte_from_exp(unsigned e) {
+  // e: biased exponent field of amax.  Non-finite blocks (e == 255) get the E8M0 NaN.
+  return e == 255u ? 255u : (e > 2u ? e - 2u : 0u);
+}
+
+// ---------------------------------------------------------------------------------
+// MXFP4 quantization.  F32 selects binary32 input (else bf16).
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
+    const void* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks,
+    int contiguous) {
+  const int tid = threadIdx.x;
+  const int q = tid & 3;                       // quarter of the block owned by this lane
+  const int64_t stride = (int64_t)gridDim.x * kBlocksPerIter;
+  for (int64_t base = (int64_t)blockIdx.x * kBlocksPerIter; base < total_blocks; base += stride) {
+    int64_t xo[kUnroll], co[kUnroll], so[kUnroll];
+    bool ok[kUnroll];
+    v4i d0[kUnroll], d1[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t b = base + u * (kThreads / 4) + (tid >> 2);
+      ok[u] = b < total_blocks;
+      if (contiguous) {
+        xo[u] = b * 32 + q * 8;
+        co[u] = b * 16 + q * 4;
+        so[u] = b;
+      } else {
+        const uint32_t bb = (uint32_t)b;
+        const uint32_t row = bb / blocks_per_row;
+        const uint32_t blk = bb - row * blocks_per_row;
+        xo[u] = (int64_t)row * ld_x + blk * 32 + q * 8;
+        co[u] = (int64_t)row * ld_codes + blk * 16 + q * 4;
+        so[u] = (int64_t)row * ld_scales + blk;
+      }
+      d0[u] = v4i{0, 0, 0, 0};
+      d1[u] = v4i{0, 0, 0, 0};
+      if (ok[u]) {
+        if (F32) {
+          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo[u]);
+          d0[u] = __builtin_nontemporal_load(p);
+          d1[u] = __builtin_nontemporal_load(p + 1);
+        } else {
+          d0[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo[u]));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      unsigned amax, e;
+      if (F32) {
+        unsigned m = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          m = max(m, (unsigned)d0[u][i] & 0x7FFFFFFFu);
+          m = max(m, (unsigned)d1[u][i] & 0x7FFFFFFFu);
+        }
+        amax = quad_max_u32(m);
+        e = amax >> 23;
+      } else {
+        v2h m = {0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          m = __builtin_elementwise_max(m, __builtin_bit_cast(v2h, (unsigned)d0[u][i] & 0x7FFF7FFFu));
+        amax = quad_max_u32(max((unsigned)m[0], (unsigned)m[1]));
+        e = amax >> 7;
+      }
+      const unsigned s = scale_byte_from_exp(e);
+      const float scale = e8m0_to_f32(s);
+      unsigned r = 0;
+      if (F32) {
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d0[u][0]), __int_as_float(d0[u][1]), scale, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d0[u][2]), __int_as_float(d0[u][3]), scale, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d1[u][0]), __int_as_float(d1[u][1]), scale, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d1[u][2]), __int_as_float(d1[u][3]), scale, 3);
+      } else {
+        // bf16 pairs are widened exactly to binary32 (a shift / a mask) and converted
+        // with the f32 form, whose destination-byte select places byte k of the word
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][0]), hi_f32(d0[u][0]), scale, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][1]), hi_f32(d0[u][1]), scale, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][2]), hi_f32(d0[u][2]), scale, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][3]), hi_f32(d0[u][3]), scale, 3);
+      }
+      if (ok[u]) {
+        *reinterpret_cast<unsigned*>(codes + co[u]) = r;
+        if (q == 0) scales[so[u]] = (uint8_t)s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Static FP8 E4M3: q = E4M3_RNE(clamp(fl32(x * inv_scale), -448, 448)).  The clamp makes
+// the gfx950 conversion saturate (it returns NaN past the rounding edge otherwise); the
+// clamp keeps the sign of zero.  16 elements per lane, one 16-byte store.
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void fp8_quantize_kernel(
+    const void* __restrict__ x, int64_t ld_x, float inv_scale, uint8_t* __restrict__ out, int64_t ld_q,
+    uint32_t chunks_per_row, int64_t total_chunks, int contiguous) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total_chunks; c += stride) {
+    int64_t xo, qo;
+    if (contiguous) {
+      xo = c * 16;
+      qo = c * 16;
+    } else {
+      const uint32_t cc = (uint32_t)c;
+      const uint32_t row = cc / chunks_per_row;
+      const uint32_t col = cc - row * chunks_per_row;
+      xo = (int64_t)row * ld_x + col * 16;
+      qo = (int64_t)row * ld_q + col * 16;
+    }
+    float v[16];
+    if (F32) {
+      const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const v4i d = __builtin_nontemporal_load(p + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[4 * i + j] = __int_as_float(d[j]);
+      }
+    } else {
+      const v4i* p = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const v4i d = __builtin_nontemporal_load(p + i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[8 * i + 2 * j] = __uint_as_float((unsigned)d[j] << 16);
+          v[8 * i + 2 * j + 1] = __uint_as_float((unsigned)d[j] & 0xFFFF0000u);
+        }
+      }
+    }
+    v4i o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float y[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_fmed3f(v[4 * i + j] * inv_scale, -448.0f, 448.0f);
+      int r = 0;
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], r, false);
+      r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+      o[i] = r;
+    }
+    __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(out + qo));
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// max |x| over a tensor (8 elements per lane per step); the result is combined with an
+// integer atomic max on the binary32 bit pattern, which orders non-negative floats.
+__global__ void absmax_init_kernel(float* out) { *out = 0.0f; }
+
+template <bool F32>
+__global__ __launch_bounds__(kThreads) void absmax_kernel(const void* __restrict__ x, int64_t ld_x,
+                                                          uint32_t chunks_per_row, int64_t total_chunks,
+                                                          int contiguous, unsigned* __restrict__ out) {
+  __shared__ unsigned red[kThreads / 64];
+  unsigned m = 0;
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total_chunks; c += stride) {
+    int64_t xo;
+    if (contiguous) {
+      xo = c * 8;
+    } else {
+      const uint32_t cc = (uint32_t)c;
+      const uint32_t row = cc / chunks_per_row;
+      xo = (int64_t)row * ld_x + (int64_t)(cc - row * chunks_per_row) * 8;
+    }
+    if (F32) {
+      const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
+      const v4i a = p[0], b = p[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m = max(m, max((unsigned)a[i] & 0x7FFFFFFFu, (unsigned)b[i] & 0x7FFFFFFFu));
+    } else {
+      const v4i a = *reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        m = max(m, max(((unsigned)a[i] & 0x7FFFu) << 16, (unsigned)a[i] & 0x7FFF0000u));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    unsigned r = red[0];
+    for (int i = 1; i < kThreads / 64; ++i) r = max(r, red[i]);
+    atomicMax(out, r);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// MXFP4 -> bf16: e2m1(code) * 2^(s - 127).  The product is formed in binary32 (exact:
+// at most 3 significant bits, exponent within binary32's range down to the subnormal
+// 2^-128) and narrowed to bf16 with round to nearest even (exact in range).
+__global__ __launch_bounds__(kThreads) void dequantize_kernel(
+    const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
+    int64_t ld_scales, uint16_t* __restrict__ y, int64_t ld_y, uint32_t blocks_per_row,
+    int64_t total_quarters) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total_quarters; g += stride) {
+    const int64_t b = g >> 2;
+    const int q = (int)(g & 3);
+    const uint32_t row = (uint32_t)(b / blocks_per_row);
+    const uint32_t blk = (uint32_t)(b - (int64_t)row * blocks_per_row);
+    const unsigned c = *reinterpret_cast<const unsigned*>(codes + (int64_t)row * ld_codes + blk * 16 + q * 4);
+    const unsigned s = scales[(int64_t)row * ld_scales + blk];
+    // 2 * |e2m1| for magnitude codes 0..7 is 0,1,2,3,4,6,8,12: one nibble each
+    const float half_scale = s >= 2 ? __uint_as_float((s - 1) << 23) : (s == 1 ? 0x1p-127f : 0x1p-128f);
+    const float sc = s == 255 ? __uint_as_float(0x7FC00000u) : half_scale;
+    v4i o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float f[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const unsigned code = (c >> (8 * i + 4 * h)) & 0xF;
+        const float mag = (float)((0xC8643210u >> (4 * (code & 7))) & 0xF) * sc;
+        f[h] = (code & 8) ? -mag : mag;
+      }
+      o[i] = (int)pack_bf16x2(f[0], f[1]);
+    }
+    *reinterpret_cast<v4i*>(y + (int64_t)row * ld_y + blk * 32 + q * 8) = o;
+  }
+}
+
+int grid_for(int64_t work_items, int64_t per_block) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  const int64_t cap = 256 * 64;  // enough resident waves to cover HBM latency
+  if (g > cap) g = cap;
+  return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
+                                 uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                                 hipStream_t stream) {
+  const int64_t bpr = cols / 32;
+  const int64_t total = rows * bpr;
+  if (total == 0) return hipSuccess;
+  const int contiguous = (ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr) ? 1 : 0;
+  const int grid = grid_for(total, kBlocksPerIter);
+  if (f32)
+    hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes,
+                       ld_codes, scales, ld_scales, (uint32_t)bpr, total, contiguous);
+  else
+    hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes,
+                       ld_codes, scales, ld_scales, (uint32_t)bpr, total, contiguous);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
+                               float inv_scale, uint8_t* q, int64_t ld_q, hipStream_t stream) {
+  const int64_t cpr = cols / 16;
+  const int64_t total = rows * cpr;
+  if (total == 0) return hipSuccess;
+  const int contiguous = (ld_x == cols && ld_q == cols) ? 1 : 0;
+  const int grid = grid_for(total, kThreads);
+  if (f32)
+    hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, inv_scale,
+                       q, ld_q, (uint32_t)cpr, total, contiguous);
+  else
+    hipLaunchKernelGGL(fp8_quantize_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, inv_scale,
+                       q, ld_q, (uint32_t)cpr, total, contiguous);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x, float* out,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL(absmax_init_kernel, dim3(1), dim3(1), 0, stream, out);
+  const int64_t cpr = cols / 8;
+  const int64_t total = rows * cpr;
+  if (total > 0) {
+    const int contiguous = ld_x == cols ? 1 : 0;
+    const int grid = grid_for(total, kThreads * 4);
+    if (f32)
+      hipLaunchKernelGGL(absmax_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, (uint32_t)cpr,
+                         total, contiguous, reinterpret_cast<unsigned*>(out));
+    else
+      hipLaunchKernelGGL(absmax_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, (uint32_t)cpr,
+                         total, contiguous, reinterpret_cast<unsigned*>(out));
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
+                             int64_t ld_scales, int64_t rows, int64_t cols, uint16_t* y, int64_t ld_y,
+                             hipStream_t stream) {
+  const int64_t bpr = cols / 32;
+  const int64_t total = rows * bpr * 4;
+  if (total == 0) return hipSuccess;
+  const int grid = grid_for(total, kThreads);
+  hipLaunchKernelGGL(dequantize_kernel, dim3(grid), dim3(kThreads), 0, stream, codes, ld_codes, scales,
+                     ld_scales, y, ld_y, (uint32_t)bpr, total);
+  return hipGetLastError();
+}
+
+}  // namespace mxq

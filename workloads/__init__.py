@@ -81,11 +81,15 @@ def activations(M: int, K: int, kind: str, seed: int = 0, name: str = "custom",
 
     * "lognormal_channels": N(0, 1) * c_k with one c_k ~ LogNormal(0, 1) per K-channel
       (an outlier-channel activation model).
+    * "normal": i.i.d. N(0, 1).
     * "student_t": i.i.d. Student-t with ``nu`` degrees of freedom (heavy tails),
       drawn as Z / sqrt(G / (nu/2)) with G ~ Gamma(nu/2, 1), so 2G ~ chi^2_nu.
     The float32 draw is rounded to ``dtype`` by torch (round to nearest even).
     """
-    if kind == "lognormal_channels":
+    if kind == "normal":
+        ga = _gen(device, seed, name, "act")
+        x = torch.randn(M, K, generator=ga, device=device, dtype=torch.float32)
+    elif kind == "lognormal_channels":
         gc = _gen(device, seed, name, "channel_scale")
         c = torch.exp(torch.randn(K, generator=gc, device=device, dtype=torch.float32))
         ga = _gen(device, seed, name, "act")
