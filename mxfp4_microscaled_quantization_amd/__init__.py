@@ -4,7 +4,7 @@ The functions here only marshal arguments: they check tensor devices, dtypes and
 allocate outputs with torch (device memory) and call the C ABI declared in
 ``include/mxq.h`` on torch's current HIP stream.  Every step of the computation runs in
 the library's gfx950 kernels.  Importing fails loudly if ``libmxq.so`` has not been
-built (``python -m mxfp4_microscaled_quantization_amd.build``); there is no fallback.
+built (``python mxfp4_microscaled_quantization_amd/build.py``); there is no fallback.
 
 Function names mirror the C entry points without the ``mxq_`` prefix:
 ``quantize``, ``quantize_fp8``, ``absmax``, ``gemm_w4a4``, ``gemm_w4a8``, ``gemm_bf16``,
@@ -50,7 +50,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"libmxq.so not found at {LIB_PATH}; build it with "
-            "`python -m mxfp4_microscaled_quantization_amd.build` (hipcc, gfx950)")
+            "`python mxfp4_microscaled_quantization_amd/build.py` (hipcc, gfx950)")
     handle = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in ABI_SYMBOLS.items():
         fn = getattr(handle, name)

@@ -1,6 +1,8 @@
 """Build libmxq.so for gfx950 in-tree with hipcc.
 
-    python -m mxfp4_microscaled_quantization_amd.build [--verbose]
+    python mxfp4_microscaled_quantization_amd/build.py [--verbose]
+
+(run as a script: importing the package would load the library being rebuilt)
 
 All HIP sources under csrc/ are compiled into one shared library next to this file.
 Packed-FP32 VALU instructions are disabled (-packed-fp32-ops); no fast-math.
@@ -45,6 +47,11 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+    # a kernel whose host stub was not emitted leaves an undefined symbol behind
+    und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
+    bad = [ln for ln in und.splitlines() if "__device_stub__" in ln]
+    if bad:
+        raise RuntimeError("kernel host stubs missing from the build:\n" + "\n".join(bad))
     os.replace(tmp, LIB)
     return LIB
 

@@ -17,7 +17,8 @@
 //    every lane finishes holding 4 consecutive output columns of one row (8-byte stores).
 //  * K advances in windows of 128 bytes per row (256 fp4 / 128 fp8 / 64 bf16 values).
 //    Each window is staged global -> registers -> LDS, double buffered (2 x 64 KB), with
-//    16-byte chunks XOR-swizzled by row so MFMA fragment reads are bank-conflict free.
+//    16-byte chunks XOR-swizzled by row so MFMA fragment reads are bank-conflict free
+//    (the fast path streams global -> LDS directly with buffer_load ... lds).
 //  * Inside a window the MFMA K-slots are assigned so that lane group g (lanes 32g..32g+31)
 //    at MFMA step t holds K-block 4g+t (fp4): a lane reads contiguous 16-byte chunks and
 //    one 32-bit word holds its four scale bytes, selected by op_sel = t.  Any assignment
@@ -27,6 +28,8 @@
 //  * Workgroups are renumbered so that each XCD (dispatched round-robin) walks a
 //    contiguous run of tiles, grouped 4 m-tiles wide, keeping panels shared in its L2.
 //  * Ragged M/N/K tails are zero-filled by buffer-load range checks and masked stores.
+#include <type_traits>
+
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -64,11 +67,16 @@ struct Params {
   int scale_dword_ok;
 };
 
+// LDS swizzles.  The LDS serves a ds_read_b128 16 lanes at a time over 64 4-byte banks
+// (256 bytes); fragment reads have 16 consecutive lanes on 16 consecutive rows at one
+// logical chunk, so the 16-byte slot of chunk c in row r is c ^ f(r) with f distinct
+// over the rows that share banks: 128-byte rows pair up per 256 bytes (f = (r>>1)&7),
+// 64-byte rows quarter it (f = (r>>2)&3).
 __device__ __forceinline__ uint32_t swz128(uint32_t row, uint32_t chunk) {
-  return row * 128u + ((chunk ^ (row & 7u)) << 4);
+  return row * 128u + ((chunk ^ ((row >> 1) & 7u)) << 4);
 }
 __device__ __forceinline__ uint32_t swz64(uint32_t row, uint32_t chunk) {
-  return row * 64u + ((chunk ^ ((row >> 1) & 3u)) << 4);
+  return row * 64u + ((chunk ^ ((row >> 2) & 3u)) << 4);
 }
 
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
@@ -145,7 +153,7 @@ __device__ __forceinline__ void mfma_step(v16f (&acc)[4][4], const uint8_t* lds_
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p) {
+__global__ __launch_bounds__(NT, 1) void gemm_generic_kernel(Params p) {
   using C = Cfg<MODE>;
   constexpr uint32_t A_TILE = BM * C::A_RB;
   constexpr uint32_t W_TILE = BN * C::W_RB;
@@ -310,6 +318,315 @@ __global__ __launch_bounds__(NT, 1) void gemm_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// Fast path: K is a whole number of windows and scale rows are 4-byte multiples (every
+// workload shape).  Tiles stream global -> LDS with buffer_load ... lds (no staging
+// registers); each wave issues whole 1 KB LDS lines whose lanes fetch the chunk the XOR
+// swizzle places there.  One barrier per window; the next window's loads and its first
+// fragment reads are issued under the current window's last MFMA step.
+// buffer_load_dword ... lds: 4 bytes per lane into LDS at `lds_line` + 4 * lane
+__device__ __forceinline__ void load_dword_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_line, uint32_t voff,
+                                                  uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_line, 4, voff, soff, 0, 0);
+}
+
+// buffer_load_dwordx4 ... lds: 16 bytes per lane into LDS at `lds_line` + 16 * lane
+__device__ __forceinline__ void load_line_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_line, uint32_t voff,
+                                                 uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_line, 16, voff, soff, 0, 0);
+}
+
+template <int MODE>
+__device__ __forceinline__ void read_frags(v4i (&f)[12], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
+                                           uint32_t lane, int t) {
+  const uint32_t g = lane >> 5, r32 = lane & 31;
+  if constexpr (MODE == GEMM_W4A8) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f[i] = *reinterpret_cast<const v4i*>(lw + swz64(wn * 128 + 32 * i + r32, 2 * g + t));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = wm * 128 + 32 * j + r32;
+      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 2 * t + g));
+      f[8 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 4 + 2 * t + g));
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      f[i] = *reinterpret_cast<const v4i*>(lw + swz128(wn * 128 + 32 * i + r32, 4 * g + t));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(wm * 128 + 32 * j + r32, 4 * g + t));
+  }
+}
+
+template <int MODE, int T>
+__device__ __forceinline__ void mfma16(v16f (&acc)[4][4], const v4i (&f)[12], const uint32_t (&scw)[4],
+                                       const uint32_t (&sca)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (MODE == GEMM_W4A4)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), widen(f[4 + j]), acc[i][j], 4, 4, T,
+                                                                    (int)scw[i], T, (int)sca[j]);
+      else if constexpr (MODE == GEMM_W4A8)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), cat(f[4 + j], f[8 + j]), acc[i][j],
+                                                                    4, 0, T, (int)scw[i], 0, 127);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                            __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
+  using C = Cfg<MODE>;
+  constexpr uint32_t A_TILE = BM * C::A_RB;
+  constexpr uint32_t W_TILE = BN * C::W_RB;
+  // scale bytes per row per window (W4A4: 8 blocks, W4A8: 4 blocks, bf16: none)
+  constexpr uint32_t SC_WIN = (MODE == GEMM_W4A4) ? 8 : (MODE == GEMM_W4A8 ? 4 : 0);
+  constexpr uint32_t SW_TILE = BN * SC_WIN;
+  constexpr uint32_t SA_TILE = (MODE == GEMM_W4A4) ? BM * SC_WIN : 0;
+  constexpr uint32_t BUF = A_TILE + W_TILE + SW_TILE + SA_TILE;
+  constexpr int A_LINES = A_TILE / 1024 / 4;   // 1 KB LDS lines per wave per window
+  constexpr int W_LINES = W_TILE / 1024 / 4;
+  constexpr int SW_LINES = SW_TILE / 256 / 4;  // 256-byte lines (4-byte DMA) per wave
+  constexpr int SA_LINES = SA_TILE / 256 / 4;
+  constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
+  constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const uint32_t wm = wave & 1, wn = wave >> 1;
+
+  const int nt = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q8 = nt >> 3, r8 = nt & 7;
+  const int seq = xcd * q8 + min(xcd, r8) + local;
+  const int group = seq / (GROUP_M * p.tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(GROUP_M, p.tiles_m - first_m);
+  const int in_group = seq - group * GROUP_M * p.tiles_n;
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
+  const bool has_ws = MODE != GEMM_BF16, has_as = MODE == GEMM_W4A4;
+  const __amdgpu_buffer_rsrc_t rsw =
+      make_rsrc(has_ws ? p.w_scales + (int64_t)n0 * p.scale_row_bytes : p.w, has_ws ? rows_w * p.scale_row_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc(has_as ? p.a_scales + (int64_t)m0 * p.scale_row_bytes : p.a, has_as ? rows_a * p.scale_row_bytes : 0);
+
+  // Lane geometry of the direct-to-LDS tile loads: LDS line q holds rows
+  // [q * ROWS_PER_LINE, ...); lane i lands at byte 16 i of the line, i.e. in row i / CPR at
+  // slot i % CPR, and fetches the chunk the swizzle maps there.  With 128-byte rows the
+  // swizzle term (r>>1)&7 depends on the line's parity: one offset for even lines, one
+  // for odd lines.
+  constexpr uint32_t A_CPR = C::A_RB / 16, W_CPR = C::W_RB / 16;
+  const uint32_t a_row = lane / A_CPR, a_slot = lane % A_CPR;           // A_RB == 128
+  const uint32_t a_voff0 = a_row * p.a_row_bytes + ((a_slot ^ ((a_row >> 1) & 7u)) * 16);
+  const uint32_t a_voff1 = a_row * p.a_row_bytes + ((a_slot ^ ((8u + a_row) >> 1 & 7u)) * 16);
+  const uint32_t w_row = lane / W_CPR, w_slot = lane % W_CPR;
+  uint32_t w_voff0, w_voff1;
+  if constexpr (C::W_RB == 128) {
+    w_voff0 = w_row * p.w_row_bytes + ((w_slot ^ ((w_row >> 1) & 7u)) * 16);
+    w_voff1 = w_row * p.w_row_bytes + ((w_slot ^ ((8u + w_row) >> 1 & 7u)) * 16);
+  } else {                                                              // 16 rows per line
+    w_voff0 = w_voff1 = w_row * p.w_row_bytes + ((w_slot ^ ((w_row >> 2) & 3u)) * 16);
+  }
+  // Scale planes are staged per window as [row][SC_WIN bytes] with 4-byte DMA: dword d of
+  // the plane is row d / (SC_WIN/4), word d % (SC_WIN/4).
+  constexpr uint32_t SC_WORDS = SC_WIN / 4 > 0 ? SC_WIN / 4 : 1;
+  const uint32_t sc_voff = (lane / SC_WORDS) * p.scale_row_bytes + (lane % SC_WORDS) * 4;
+  constexpr uint32_t SC_ROWS_PER_LINE = 64 / SC_WORDS;
+
+  auto issue_loads = [&](int w, uint32_t stage) {
+    uint8_t* la = lds + stage;
+    uint8_t* lw = la + A_TILE;
+#pragma unroll
+    for (int j = 0; j < A_LINES; ++j) {
+      const uint32_t line = wave * A_LINES + j;
+      load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+                       (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
+    }
+#pragma unroll
+    for (int j = 0; j < W_LINES; ++j) {
+      const uint32_t line = wave * W_LINES + j;
+      load_line_to_lds(rw, lw + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+                       (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
+    }
+    if constexpr (SC_WIN > 0) {
+      uint8_t* lsw = lw + W_TILE;
+#pragma unroll
+      for (int j = 0; j < SW_LINES; ++j) {
+        const uint32_t line = wave * SW_LINES + j;
+        load_dword_to_lds(rsw, lsw + line * 256, sc_voff, (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
+      }
+      if constexpr (SA_TILE > 0) {
+        uint8_t* lsa = lsw + SW_TILE;
+#pragma unroll
+        for (int j = 0; j < SA_LINES; ++j) {
+          const uint32_t line = wave * SA_LINES + j;
+          load_dword_to_lds(rsa, lsa + line * 256, sc_voff,
+                            (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
+        }
+      }
+    }
+  };
+  // this lane's scale words for the window in `stage`: W rows (4 n-fragments), A rows
+  // (4 m-fragments); W4A4 lane group g owns blocks 4g..4g+3 (word g), W4A8 blocks 2g, 2g+1
+  auto read_scales = [&](uint32_t stage, uint32_t (&scw)[4], uint32_t (&sca)[4]) {
+    if constexpr (SC_WIN > 0) {
+      const uint8_t* lsw = lds + stage + A_TILE + W_TILE;
+      const uint32_t g = lane >> 5, r32 = lane & 31;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t row = wn * 128 + 32 * i + r32;
+        if constexpr (MODE == GEMM_W4A4)
+          scw[i] = *reinterpret_cast<const uint32_t*>(lsw + row * SC_WIN + 4 * g);
+        else
+          scw[i] = *reinterpret_cast<const uint32_t*>(lsw + row * SC_WIN) >> (16 * g);
+      }
+      if constexpr (SA_TILE > 0) {
+        const uint8_t* lsa = lsw + SW_TILE;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          sca[j] = *reinterpret_cast<const uint32_t*>(lsa + (wm * 128 + 32 * j + r32) * SC_WIN + 4 * g);
+      }
+    }
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nwin = p.nwin;
+  uint32_t scw[4] = {0, 0, 0, 0}, sca[4] = {0, 0, 0, 0};
+  v4i f0[12], f1[12];
+  constexpr int RD = (MODE == GEMM_W4A8) ? 12 : 8;       // ds_read_b128 per fragment set
+  constexpr int VM = A_LINES + W_LINES + SW_LINES + SA_LINES;   // LDS-DMA loads per wave per window
+  constexpr int SR = (MODE == GEMM_W4A4) ? 8 : (MODE == GEMM_W4A8 ? 4 : 0);   // scale reads
+
+  // prologue: window 0 resident, window 1 in flight, step-0 fragments and scales read
+  issue_loads(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);          // vmcnt/lgkmcnt = 0: stage 0 written
+  __syncthreads();
+  if (nwin > 1) issue_loads(1, BUF);
+  read_frags<MODE>(f0, lds, lds + A_TILE, wm, wn, lane, 0);
+  read_scales(0, scw, sca);
+
+  for (int w = 0; w < nwin; ++w) {
+    const uint32_t cur = (uint32_t)(w & 1) * BUF;
+    const uint8_t* la = lds + cur;
+    const uint8_t* lw = la + A_TILE;
+    // steps 0 .. STEPS-2: the next step's fragments are read under this step's MFMAs
+    if constexpr (C::STEPS == 4) {
+      read_frags<MODE>(f1, la, lw, wm, wn, lane, 1);
+      mfma16<MODE, 0>(acc, f0, scw, sca);
+      read_frags<MODE>(f0, la, lw, wm, wn, lane, 2);
+      mfma16<MODE, 1>(acc, f1, scw, sca);
+      read_frags<MODE>(f1, la, lw, wm, wn, lane, 3);
+      mfma16<MODE, 2>(acc, f0, scw, sca);
+#pragma unroll
+      for (int k = 0; k < 3; ++k)
+#pragma unroll
+        for (int r = 0; r < RD; ++r) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+        }
+    } else {
+      read_frags<MODE>(f1, la, lw, wm, wn, lane, 1);
+      mfma16<MODE, 0>(acc, f0, scw, sca);
+#pragma unroll
+      for (int r = 0; r < RD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 16 - RD, 0);
+    }
+    // Hand-over, kept on this side of the last step's MFMAs (which touch no memory and
+    // would otherwise be sunk below the barrier, exposing the LDS reads): wait for this
+    // wave's LDS reads and for window w+1, then let every wave pass stage `cur`, refill it
+    // with window w+2 and read window w+1's first fragments and scales.
+    // (unconditional except the prefetch: on the last window the reads are of a stage that
+    // is not used again, which keeps the fragment registers free of loop-carried copies)
+    uint32_t scw_n[4], sca_n[4];
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    if (w + 2 < nwin) issue_loads(w + 2, cur);
+    read_frags<MODE>(f0, lds + (cur ^ BUF), lds + (cur ^ BUF) + A_TILE, wm, wn, lane, 0);
+    read_scales(cur ^ BUF, scw_n, sca_n);
+    if constexpr (C::STEPS == 4)
+      mfma16<MODE, 3>(acc, f1, scw, sca);
+    else
+      mfma16<MODE, 1>(acc, f1, scw, sca);
+#pragma unroll
+    for (int k = 0; k < VM / 2; ++k) {
+      __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);     // 2 VMEM (LDS-DMA) loads
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // 1 MFMA
+    }
+#pragma unroll
+    for (int r = 0; r < RD + SR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      scw[i] = scw_n[i];
+      sca[i] = sca_n[i];
+    }
+  }
+
+  // ---- epilogue: fp32 -> bf16 (RNE); a lane owns 4 consecutive columns per store ----
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+  const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + (int)(wm * 128 + 32 * j + r32);
+    uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
+        float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+        float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+        if constexpr (MODE == GEMM_W4A8) {
+          v0 *= p.a_scale;
+          v1 *= p.a_scale;
+          v2 *= p.a_scale;
+          v3 *= p.a_scale;
+        }
+        const unsigned lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
+        if (full) {
+          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+        } else if (m < p.M) {
+          if (p.vec_store && n + 4 <= p.N) {
+            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+          } else {
+            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
+            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
+            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
+            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
+          }
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,
@@ -332,22 +649,33 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
   p.tiles_m = (int)((M + BM - 1) / BM);
   p.tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(NT);
+  // the fast path needs whole windows (and, with scales, 4-byte scale rows)
+  const bool scales_ok = (K / 32) % 4 == 0;
   switch (mode) {
     case GEMM_W4A4:
       p.a_row_bytes = p.w_row_bytes = (uint32_t)(K / 2);
       p.nwin = (int)((K + Cfg<GEMM_W4A4>::K_WIN - 1) / Cfg<GEMM_W4A4>::K_WIN);
-      hipLaunchKernelGGL(gemm_kernel<GEMM_W4A4>, grid, block, 0, stream, p);
+      if (K > 0 && K % Cfg<GEMM_W4A4>::K_WIN == 0 && scales_ok)
+        hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A4>, grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL(gemm_generic_kernel<GEMM_W4A4>, grid, block, 0, stream, p);
       break;
     case GEMM_W4A8:
       p.a_row_bytes = (uint32_t)K;
       p.w_row_bytes = (uint32_t)(K / 2);
       p.nwin = (int)((K + Cfg<GEMM_W4A8>::K_WIN - 1) / Cfg<GEMM_W4A8>::K_WIN);
-      hipLaunchKernelGGL(gemm_kernel<GEMM_W4A8>, grid, block, 0, stream, p);
+      if (K > 0 && K % Cfg<GEMM_W4A8>::K_WIN == 0 && scales_ok)
+        hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A8>, grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL(gemm_generic_kernel<GEMM_W4A8>, grid, block, 0, stream, p);
       break;
     case GEMM_BF16:
       p.a_row_bytes = p.w_row_bytes = (uint32_t)(K * 2);
       p.nwin = (int)((K + Cfg<GEMM_BF16>::K_WIN - 1) / Cfg<GEMM_BF16>::K_WIN);
-      hipLaunchKernelGGL(gemm_kernel<GEMM_BF16>, grid, block, 0, stream, p);
+      if (K > 0 && K % Cfg<GEMM_BF16>::K_WIN == 0)
+        hipLaunchKernelGGL(gemm_fast_kernel<GEMM_BF16>, grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL(gemm_generic_kernel<GEMM_BF16>, grid, block, 0, stream, p);
       break;
   }
   return hipGetLastError();
