@@ -42,15 +42,29 @@ constexpr int NT = 256;   // threads per workgroup
 constexpr int GROUP_M = 4;
 
 template <int MODE> struct Cfg;
+// NS: LDS stages of the fast path (a window's loads get NS-1 windows of compute to land)
 template <> struct Cfg<GEMM_W4A4> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NS = 2;
 };
 template <> struct Cfg<GEMM_W4A8> {
-  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128;
+  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NS = 3;
 };
 template <> struct Cfg<GEMM_BF16> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NS = 2;
 };
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= 0, expcnt unconstrained
+constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
+
+// Workgroup barrier for the LDS stage hand-over.  The caller has already waited (s_waitcnt)
+// for exactly the loads that must have landed; __syncthreads() would add a release fence
+// that drains every outstanding load, including the later stages still in flight.  The
+// empty asm statements keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 struct Params {
   const uint8_t* a;
@@ -395,7 +409,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   constexpr int SA_LINES = SA_TILE / 256 / 4;
   constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
   constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * BUF];
+  constexpr int NS = C::NS;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * BUF];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
@@ -516,16 +531,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   constexpr int VM = A_LINES + W_LINES + SW_LINES + SA_LINES;   // LDS-DMA loads per wave per window
   constexpr int SR = (MODE == GEMM_W4A4) ? 8 : (MODE == GEMM_W4A8 ? 4 : 0);   // scale reads
 
-  // prologue: window 0 resident, window 1 in flight, step-0 fragments and scales read
+  // prologue: window k goes to stage k % NS.  Window 0 resident, windows 1 .. NS-1 in
+  // flight, step-0 fragments and scales read.
   issue_loads(0, 0);
   __builtin_amdgcn_s_waitcnt(0);          // vmcnt/lgkmcnt = 0: stage 0 written
   __syncthreads();
-  if (nwin > 1) issue_loads(1, BUF);
+#pragma unroll
+  for (int k = 1; k < NS; ++k)
+    if (k < nwin) issue_loads(k, k * BUF);
   read_frags<MODE>(f0, lds, lds + A_TILE, wm, wn, lane, 0);
   read_scales(0, scw, sca);
 
-  for (int w = 0; w < nwin; ++w) {
-    const uint32_t cur = (uint32_t)(w & 1) * BUF;
+  // One window.  STEADY: windows w+1 .. w+NS exist, so the hand-over waits for window w+1
+  // only and refills stage `cur` with window w+NS.  Tail (last NS windows): wait for
+  // everything, load nothing.  Both are free of control flow, so nothing can be sunk past
+  // the barrier.
+  auto window = [&](int w, auto steady_tag) {
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const uint32_t cur = (uint32_t)(w % NS) * BUF;
+    const uint32_t nxt_stage = (uint32_t)((w + 1) % NS) * BUF;
     const uint8_t* la = lds + cur;
     const uint8_t* lw = la + A_TILE;
     // steps 0 .. STEPS-2: the next step's fragments are read under this step's MFMAs
@@ -554,27 +578,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       __builtin_amdgcn_sched_group_barrier(0x008, 16 - RD, 0);
     }
     // Hand-over, kept on this side of the last step's MFMAs (which touch no memory and
-    // would otherwise be sunk below the barrier, exposing the LDS reads): wait for this
-    // wave's LDS reads and for window w+1, then let every wave pass stage `cur`, refill it
-    // with window w+2 and read window w+1's first fragments and scales.
-    // (unconditional except the prefetch: on the last window the reads are of a stage that
-    // is not used again, which keeps the fragment registers free of loop-carried copies)
+    // would otherwise be moved below the barrier, exposing the LDS reads).
     uint32_t scw_n[4], sca_n[4];
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if constexpr (STEADY && NS > 2)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * VM));   // window w+1 landed
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    stage_barrier();                      // every wave is past stage `cur`
     __builtin_amdgcn_sched_barrier(0);
-    if (w + 2 < nwin) issue_loads(w + 2, cur);
-    read_frags<MODE>(f0, lds + (cur ^ BUF), lds + (cur ^ BUF) + A_TILE, wm, wn, lane, 0);
-    read_scales(cur ^ BUF, scw_n, sca_n);
+    if constexpr (STEADY) issue_loads(w + NS, cur);     // NS-1 windows ahead of its use
+    read_frags<MODE>(f0, lds + nxt_stage, lds + nxt_stage + A_TILE, wm, wn, lane, 0);
+    read_scales(nxt_stage, scw_n, sca_n);
     if constexpr (C::STEPS == 4)
       mfma16<MODE, 3>(acc, f1, scw, sca);
     else
       mfma16<MODE, 1>(acc, f1, scw, sca);
+    if constexpr (STEADY) {
 #pragma unroll
-    for (int k = 0; k < VM / 2; ++k) {
-      __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);     // 2 VMEM (LDS-DMA) loads
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);     // 1 MFMA
+      for (int k = 0; k < VM / 2; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);   // 2 VMEM (LDS-DMA) loads
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
+      }
     }
 #pragma unroll
     for (int r = 0; r < RD + SR; ++r) {
@@ -587,7 +612,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       scw[i] = scw_n[i];
       sca[i] = sca_n[i];
     }
-  }
+  };
+  int w = 0;
+  for (; w < nwin - NS; ++w) window(w, std::true_type{});
+  for (; w < nwin; ++w) window(w, std::false_type{});
 
   // ---- epilogue: fp32 -> bf16 (RNE); a lane owns 4 consecutive columns per store ----
   const uint32_t r32 = lane & 31, g = lane >> 5;
