@@ -53,6 +53,22 @@ template <> struct Cfg<GEMM_BF16> {
   static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NS = 2;
 };
 
+// Fast-path geometry.  A_RB / W_RB: bytes per row per K-window for the activation / weight
+// tile (128 bytes: whole cache lines per row); STEPS: 32x32 MFMA steps per window; NS: LDS
+// stages (a window's loads get NS-1 windows of compute to land); SC_WIN: scale bytes per row
+// per window.  Lane group g at step t holds K-chunk g * STEPS + t of the weight row (and of
+// the activation row for FP4 / bf16 activations).
+template <int MODE> struct Fast;
+template <> struct Fast<GEMM_W4A4> {
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NS = 2, SC_WIN = 8;
+};
+template <> struct Fast<GEMM_W4A8> {
+  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NS = 3, SC_WIN = 4;
+};
+template <> struct Fast<GEMM_BF16> {
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NS = 2, SC_WIN = 0;
+};
+
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= 0, expcnt unconstrained
 constexpr int waitcnt_vm(int vm) { return (vm & 0xF) | ((vm >> 4) << 14) | (0x7 << 4); }
 
@@ -91,6 +107,14 @@ __device__ __forceinline__ uint32_t swz128(uint32_t row, uint32_t chunk) {
 }
 __device__ __forceinline__ uint32_t swz64(uint32_t row, uint32_t chunk) {
   return row * 64u + ((chunk ^ ((row >> 2) & 3u)) << 4);
+}
+
+template <int RB>
+__device__ __forceinline__ uint32_t swz(uint32_t row, uint32_t chunk) {
+  if constexpr (RB == 128)
+    return swz128(row, chunk);
+  else
+    return swz64(row, chunk);
 }
 
 __device__ __forceinline__ v8i widen(v4i x) { return v8i{x[0], x[1], x[2], x[3], 0, 0, 0, 0}; }
@@ -350,14 +374,20 @@ __device__ __forceinline__ void load_line_to_lds(__amdgpu_buffer_rsrc_t r, uint8
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_line, 16, voff, soff, 0, 0);
 }
 
+// Fragments of MFMA step t from one LDS stage.  Lane group g (lanes 32g..32g+31) at step t
+// holds K-chunk g * STEPS + t of its weight row (fp4: one 32-element block; bf16: 8
+// elements) and the same chunk of its activation row; FP8 activation rows give each lane
+// the chunks 2t+g and 4+2t+g that the FP8 operand layout pairs with those FP4 blocks.
 template <int MODE>
 __device__ __forceinline__ void read_frags(v4i (&f)[12], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
                                            uint32_t lane, int t) {
+  using F = Fast<MODE>;
   const uint32_t g = lane >> 5, r32 = lane & 31;
-  if constexpr (MODE == GEMM_W4A8) {
+  const uint32_t chunk = g * F::STEPS + t;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f[i] = *reinterpret_cast<const v4i*>(lw + swz64(wn * 128 + 32 * i + r32, 2 * g + t));
+  for (int i = 0; i < 4; ++i)
+    f[i] = *reinterpret_cast<const v4i*>(lw + swz<F::W_RB>(wn * 128 + 32 * i + r32, chunk));
+  if constexpr (MODE == GEMM_W4A8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t row = wm * 128 + 32 * j + r32;
@@ -366,11 +396,8 @@ __device__ __forceinline__ void read_frags(v4i (&f)[12], const uint8_t* la, cons
     }
   } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      f[i] = *reinterpret_cast<const v4i*>(lw + swz128(wn * 128 + 32 * i + r32, 4 * g + t));
-#pragma unroll
     for (int j = 0; j < 4; ++j)
-      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(wm * 128 + 32 * j + r32, 4 * g + t));
+      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz<F::A_RB>(wm * 128 + 32 * j + r32, chunk));
   }
 }
 
@@ -395,11 +422,11 @@ __device__ __forceinline__ void mfma16(v16f (&acc)[4][4], const v4i (&f)[12], co
 
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
-  using C = Cfg<MODE>;
+  using C = Fast<MODE>;
   constexpr uint32_t A_TILE = BM * C::A_RB;
   constexpr uint32_t W_TILE = BN * C::W_RB;
-  // scale bytes per row per window (W4A4: 8 blocks, W4A8: 4 blocks, bf16: none)
-  constexpr uint32_t SC_WIN = (MODE == GEMM_W4A4) ? 8 : (MODE == GEMM_W4A8 ? 4 : 0);
+  // scale bytes per row per window (4 blocks for both scaled modes, none for bf16)
+  constexpr uint32_t SC_WIN = C::SC_WIN;
   constexpr uint32_t SW_TILE = BN * SC_WIN;
   constexpr uint32_t SA_TILE = (MODE == GEMM_W4A4) ? BM * SC_WIN : 0;
   constexpr uint32_t BUF = A_TILE + W_TILE + SW_TILE + SA_TILE;
@@ -443,47 +470,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // swizzle term (r>>1)&7 depends on the line's parity: one offset for even lines, one
   // for odd lines.
   constexpr uint32_t A_CPR = C::A_RB / 16, W_CPR = C::W_RB / 16;
-  const uint32_t a_row = lane / A_CPR, a_slot = lane % A_CPR;           // A_RB == 128
-  const uint32_t a_voff0 = a_row * p.a_row_bytes + ((a_slot ^ ((a_row >> 1) & 7u)) * 16);
-  const uint32_t a_voff1 = a_row * p.a_row_bytes + ((a_slot ^ ((8u + a_row) >> 1 & 7u)) * 16);
-  const uint32_t w_row = lane / W_CPR, w_slot = lane % W_CPR;
-  uint32_t w_voff0, w_voff1;
-  if constexpr (C::W_RB == 128) {
-    w_voff0 = w_row * p.w_row_bytes + ((w_slot ^ ((w_row >> 1) & 7u)) * 16);
-    w_voff1 = w_row * p.w_row_bytes + ((w_slot ^ ((8u + w_row) >> 1 & 7u)) * 16);
-  } else {                                                              // 16 rows per line
-    w_voff0 = w_voff1 = w_row * p.w_row_bytes + ((w_slot ^ ((w_row >> 2) & 3u)) * 16);
-  }
+  auto dma_voffs = [&](uint32_t cpr, uint32_t row_bytes, uint32_t& even, uint32_t& odd) {
+    const uint32_t row = lane / cpr, slot = lane % cpr;
+    if (cpr == 8) {                       // 128-byte rows: 8 per line, term (r>>1)&7
+      even = row * row_bytes + ((slot ^ ((row >> 1) & 7u)) * 16);
+      odd = row * row_bytes + ((slot ^ (((8u + row) >> 1) & 7u)) * 16);
+    } else {                              // 64-byte rows: 16 per line, term (r>>2)&3
+      even = odd = row * row_bytes + ((slot ^ ((row >> 2) & 3u)) * 16);
+    }
+  };
+  uint32_t a_voff0, a_voff1, w_voff0, w_voff1;
+  dma_voffs(A_CPR, p.a_row_bytes, a_voff0, a_voff1);
+  dma_voffs(W_CPR, p.w_row_bytes, w_voff0, w_voff1);
   // Scale planes are staged per window as [row][SC_WIN bytes] with 4-byte DMA: dword d of
   // the plane is row d / (SC_WIN/4), word d % (SC_WIN/4).
   constexpr uint32_t SC_WORDS = SC_WIN / 4 > 0 ? SC_WIN / 4 : 1;
   const uint32_t sc_voff = (lane / SC_WORDS) * p.scale_row_bytes + (lane % SC_WORDS) * 4;
   constexpr uint32_t SC_ROWS_PER_LINE = 64 / SC_WORDS;
 
-  auto issue_loads = [&](int w, uint32_t stage) {
+  // A window's loads in two parts, issued under different MFMA steps so that the four
+  // waves never queue a whole window of DMA at once: part 0 = activation tile and its
+  // scales, part 1 = weight tile and its scales.
+  auto issue_part = [&](int w, uint32_t stage, auto part_tag) {
+    constexpr int PART = decltype(part_tag)::value;
     uint8_t* la = lds + stage;
     uint8_t* lw = la + A_TILE;
+    uint8_t* lsw = lw + W_TILE;
+    uint8_t* lsa = lsw + SW_TILE;
+    if constexpr (PART == 0) {
 #pragma unroll
-    for (int j = 0; j < A_LINES; ++j) {
-      const uint32_t line = wave * A_LINES + j;
-      load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
-                       (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
-    }
-#pragma unroll
-    for (int j = 0; j < W_LINES; ++j) {
-      const uint32_t line = wave * W_LINES + j;
-      load_line_to_lds(rw, lw + line * 1024, (line & 1) ? w_voff1 : w_voff0,
-                       (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
-    }
-    if constexpr (SC_WIN > 0) {
-      uint8_t* lsw = lw + W_TILE;
-#pragma unroll
-      for (int j = 0; j < SW_LINES; ++j) {
-        const uint32_t line = wave * SW_LINES + j;
-        load_dword_to_lds(rsw, lsw + line * 256, sc_voff, (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
+      for (int j = 0; j < A_LINES; ++j) {
+        const uint32_t line = wave * A_LINES + j;
+        load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+                         (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
       }
       if constexpr (SA_TILE > 0) {
-        uint8_t* lsa = lsw + SW_TILE;
 #pragma unroll
         for (int j = 0; j < SA_LINES; ++j) {
           const uint32_t line = wave * SA_LINES + j;
@@ -491,27 +512,43 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
                             (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
         }
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < W_LINES; ++j) {
+        const uint32_t line = wave * W_LINES + j;
+        load_line_to_lds(rw, lw + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+                         (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
+      }
+      if constexpr (SC_WIN > 0) {
+#pragma unroll
+        for (int j = 0; j < SW_LINES; ++j) {
+          const uint32_t line = wave * SW_LINES + j;
+          load_dword_to_lds(rsw, lsw + line * 256, sc_voff,
+                            (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
+        }
+      }
     }
   };
-  // this lane's scale words for the window in `stage`: W rows (4 n-fragments), A rows
-  // (4 m-fragments); W4A4 lane group g owns blocks 4g..4g+3 (word g), W4A8 blocks 2g, 2g+1
+  auto issue_loads = [&](int w, uint32_t stage) {
+    issue_part(w, stage, std::integral_constant<int, 0>{});
+    issue_part(w, stage, std::integral_constant<int, 1>{});
+  };
+  // this lane's scale bytes for the window in `stage`: W rows (4 n-fragments), A rows
+  // (4 m-fragments); byte t is the block of MFMA step t (op_sel t)
   auto read_scales = [&](uint32_t stage, uint32_t (&scw)[4], uint32_t (&sca)[4]) {
     if constexpr (SC_WIN > 0) {
+      // lane group g's blocks g*STEPS .. g*STEPS+STEPS-1 as bytes 0.. of one word
       const uint8_t* lsw = lds + stage + A_TILE + W_TILE;
       const uint32_t g = lane >> 5, r32 = lane & 31;
+      const uint32_t word = (SC_WIN == 8) ? 4 * g : 0, sh = (SC_WIN == 8) ? 0 : 16 * g;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t row = wn * 128 + 32 * i + r32;
-        if constexpr (MODE == GEMM_W4A4)
-          scw[i] = *reinterpret_cast<const uint32_t*>(lsw + row * SC_WIN + 4 * g);
-        else
-          scw[i] = *reinterpret_cast<const uint32_t*>(lsw + row * SC_WIN) >> (16 * g);
-      }
+      for (int i = 0; i < 4; ++i)
+        scw[i] = *reinterpret_cast<const uint32_t*>(lsw + (wn * 128 + 32 * i + r32) * SC_WIN + word) >> sh;
       if constexpr (SA_TILE > 0) {
         const uint8_t* lsa = lsw + SW_TILE;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sca[j] = *reinterpret_cast<const uint32_t*>(lsa + (wm * 128 + 32 * j + r32) * SC_WIN + 4 * g);
+          sca[j] = *reinterpret_cast<const uint32_t*>(lsa + (wm * 128 + 32 * j + r32) * SC_WIN + word) >> sh;
       }
     }
   };
@@ -529,6 +566,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   v4i f0[12], f1[12];
   constexpr int RD = (MODE == GEMM_W4A8) ? 12 : 8;       // ds_read_b128 per fragment set
   constexpr int VM = A_LINES + W_LINES + SW_LINES + SA_LINES;   // LDS-DMA loads per wave per window
+  constexpr int VM0 = A_LINES + SA_LINES, VM1 = W_LINES + SW_LINES;  // per part
   constexpr int SR = (MODE == GEMM_W4A4) ? 8 : (MODE == GEMM_W4A8 ? 4 : 0);   // scale reads
 
   // prologue: window k goes to stage k % NS.  Window 0 resident, windows 1 .. NS-1 in
@@ -542,16 +580,20 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   read_frags<MODE>(f0, lds, lds + A_TILE, wm, wn, lane, 0);
   read_scales(0, scw, sca);
 
-  // One window.  STEADY: windows w+1 .. w+NS exist, so the hand-over waits for window w+1
-  // only and refills stage `cur` with window w+NS.  Tail (last NS windows): wait for
-  // everything, load nothing.  Both are free of control flow, so nothing can be sunk past
-  // the barrier.
-  auto window = [&](int w, auto steady_tag) {
+  // One window.  STEADY: windows w+1 .. w+NS exist; the hand-over waits for window w+1 only
+  // and, once every wave is past stage `cur`, refills it with part 0 of window w+NS.
+  // PEND: part 1 of window w+NS-1 (whose part 0 went out after the previous barrier) is
+  // issued under this window's step-0 MFMAs.  The tail (last NS windows) waits for
+  // everything and loads nothing.  No control flow inside, so nothing can be sunk past the
+  // barrier.
+  auto window = [&](int w, auto pend_tag, auto steady_tag) {
+    constexpr bool PEND = decltype(pend_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
     const uint32_t cur = (uint32_t)(w % NS) * BUF;
     const uint32_t nxt_stage = (uint32_t)((w + 1) % NS) * BUF;
     const uint8_t* la = lds + cur;
     const uint8_t* lw = la + A_TILE;
+    if constexpr (PEND) issue_part(w + NS - 1, (uint32_t)((w + NS - 1) % NS) * BUF, std::integral_constant<int, 1>{});
     // steps 0 .. STEPS-2: the next step's fragments are read under this step's MFMAs
     if constexpr (C::STEPS == 4) {
       read_frags<MODE>(f1, la, lw, wm, wn, lane, 1);
@@ -560,12 +602,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       mfma16<MODE, 1>(acc, f1, scw, sca);
       read_frags<MODE>(f1, la, lw, wm, wn, lane, 3);
       mfma16<MODE, 2>(acc, f0, scw, sca);
+      // step 0: its 16 MFMAs cover the next step's reads and the pending loads
 #pragma unroll
-      for (int k = 0; k < 3; ++k)
+      for (int r = 0; r < RD; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // 1 DS read
+        if (PEND && r < VM1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // 2 MFMA
+      }
+#pragma unroll
+      for (int k = 1; k < 3; ++k)
 #pragma unroll
         for (int r = 0; r < RD; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // 1 DS read
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // 2 MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         }
     } else {
       read_frags<MODE>(f1, la, lw, wm, wn, lane, 1);
@@ -573,6 +622,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
 #pragma unroll
       for (int r = 0; r < RD; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (PEND && r < VM1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(0x008, 16 - RD, 0);
@@ -587,7 +637,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       __builtin_amdgcn_s_waitcnt(0);
     stage_barrier();                      // every wave is past stage `cur`
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (STEADY) issue_loads(w + NS, cur);     // NS-1 windows ahead of its use
+    if constexpr (STEADY) issue_part(w + NS, cur, std::integral_constant<int, 0>{});
     read_frags<MODE>(f0, lds + nxt_stage, lds + nxt_stage + A_TILE, wm, wn, lane, 0);
     read_scales(nxt_stage, scw_n, sca_n);
     if constexpr (C::STEPS == 4)
@@ -596,8 +646,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       mfma16<MODE, 1>(acc, f1, scw, sca);
     if constexpr (STEADY) {
 #pragma unroll
-      for (int k = 0; k < VM / 2; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 2, 1);   // 2 VMEM (LDS-DMA) loads
+      for (int k = 0; k < VM0; ++k) {
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 VMEM (LDS-DMA) load
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
       }
     }
@@ -613,9 +663,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       sca[i] = sca_n[i];
     }
   };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
   int w = 0;
-  for (; w < nwin - NS; ++w) window(w, std::true_type{});
-  for (; w < nwin; ++w) window(w, std::false_type{});
+  if (nwin > NS) {
+    window(0, F_{}, T_{});
+    for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{});
+    window(w, T_{}, F_{});
+    ++w;
+  }
+  for (; w < nwin; ++w) window(w, F_{}, F_{});
 
   // ---- epilogue: fp32 -> bf16 (RNE); a lane owns 4 consecutive columns per store ----
   const uint32_t r32 = lane & 31, g = lane >> 5;
@@ -679,31 +736,27 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(NT);
   // the fast path needs whole windows (and, with scales, 4-byte scale rows)
   const bool scales_ok = (K / 32) % 4 == 0;
+  auto launch = [&](auto mode_tag, uint32_t a_row_bytes, uint32_t w_row_bytes, bool needs_scales) {
+    constexpr int MD = decltype(mode_tag)::value;
+    p.a_row_bytes = a_row_bytes;
+    p.w_row_bytes = w_row_bytes;
+    if (K > 0 && K % Fast<MD>::K_WIN == 0 && (scales_ok || !needs_scales)) {
+      p.nwin = (int)(K / Fast<MD>::K_WIN);
+      hipLaunchKernelGGL(gemm_fast_kernel<MD>, grid, block, 0, stream, p);
+    } else {
+      p.nwin = (int)((K + Cfg<MD>::K_WIN - 1) / Cfg<MD>::K_WIN);
+      hipLaunchKernelGGL(gemm_generic_kernel<MD>, grid, block, 0, stream, p);
+    }
+  };
   switch (mode) {
     case GEMM_W4A4:
-      p.a_row_bytes = p.w_row_bytes = (uint32_t)(K / 2);
-      p.nwin = (int)((K + Cfg<GEMM_W4A4>::K_WIN - 1) / Cfg<GEMM_W4A4>::K_WIN);
-      if (K > 0 && K % Cfg<GEMM_W4A4>::K_WIN == 0 && scales_ok)
-        hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A4>, grid, block, 0, stream, p);
-      else
-        hipLaunchKernelGGL(gemm_generic_kernel<GEMM_W4A4>, grid, block, 0, stream, p);
+      launch(std::integral_constant<int, GEMM_W4A4>{}, (uint32_t)(K / 2), (uint32_t)(K / 2), true);
       break;
     case GEMM_W4A8:
-      p.a_row_bytes = (uint32_t)K;
-      p.w_row_bytes = (uint32_t)(K / 2);
-      p.nwin = (int)((K + Cfg<GEMM_W4A8>::K_WIN - 1) / Cfg<GEMM_W4A8>::K_WIN);
-      if (K > 0 && K % Cfg<GEMM_W4A8>::K_WIN == 0 && scales_ok)
-        hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A8>, grid, block, 0, stream, p);
-      else
-        hipLaunchKernelGGL(gemm_generic_kernel<GEMM_W4A8>, grid, block, 0, stream, p);
+      launch(std::integral_constant<int, GEMM_W4A8>{}, (uint32_t)K, (uint32_t)(K / 2), true);
       break;
     case GEMM_BF16:
-      p.a_row_bytes = p.w_row_bytes = (uint32_t)(K * 2);
-      p.nwin = (int)((K + Cfg<GEMM_BF16>::K_WIN - 1) / Cfg<GEMM_BF16>::K_WIN);
-      if (K > 0 && K % Cfg<GEMM_BF16>::K_WIN == 0)
-        hipLaunchKernelGGL(gemm_fast_kernel<GEMM_BF16>, grid, block, 0, stream, p);
-      else
-        hipLaunchKernelGGL(gemm_generic_kernel<GEMM_BF16>, grid, block, 0, stream, p);
+      launch(std::integral_constant<int, GEMM_BF16>{}, (uint32_t)(K * 2), (uint32_t)(K * 2), false);
       break;
   }
   return hipGetLastError();
