@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="wan_ffn_down_sqnr")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=768, help="activation rows in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=4096, help="activation rows in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
@@ -192,20 +192,21 @@ def main():
     step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]))
     ms_per_step = wall * 1e3 / args.steps
 
+    src_keys = {"mxq_quantize": ("quantize.hip",), "mxq_quantize_fp8": ("quantize.hip",),
+                "mxq_gemm_w4a4": ("gemm.hip",), "mxq_gemm_w4a8": ("gemm.hip",), "mxq_gemm_bf16": ("gemm.hip",),
+                "mxq_sqnr_w4a4": ("sqnr.hip",), "mxq_sqnr_w4a8": ("sqnr.hip",)}
     kinfo = {}
     for name, ms in per_kernel_ms.items():
         amount, unit, peak, bound = work[name]
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
+        prof_name = "mxq_sqnr" if name.startswith("mxq_sqnr") else name
         kinfo[name] = {"ms": round(ms, 4), "achieved": round(rate, 2), "unit": unit, "peak": peak,
-                       "frac": round(rate / peak, 4), "bound": bound}
+                       "frac": round(rate / peak, 4), "bound": bound,
+                       "traffic": _traffic_from_profile(f"{prof_name}_{args.workload}", _src_hash(*src_keys[name]))}
     dominant = max(per_kernel_ms, key=per_kernel_ms.get)
-    src_keys = {"mxq_quantize": ("quantize.hip",), "mxq_quantize_fp8": ("quantize.hip",),
-                "mxq_gemm_w4a4": ("gemm.hip",), "mxq_gemm_w4a8": ("gemm.hip",), "mxq_gemm_bf16": ("gemm.hip",),
-                "mxq_sqnr_w4a4": ("sqnr.hip",), "mxq_sqnr_w4a8": ("sqnr.hip",)}
     d = kinfo[dominant]
     roofline = {"kernel": dominant, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
-                "unit": d["unit"], "frac": d["frac"],
-                "traffic": _traffic_from_profile(f"{dominant}_{args.workload}", _src_hash(*src_keys[dominant]))}
+                "unit": d["unit"], "frac": d["frac"], "traffic": d["traffic"]}
 
     res = {
         "metric": "W4A4/W4A8 GEMM TFLOP/s (% of MXFP4/FP8 peak); quantize GB/s (% of HBM)",
