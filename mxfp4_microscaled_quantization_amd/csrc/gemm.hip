@@ -378,28 +378,47 @@ __device__ __forceinline__ void load_line_to_lds(__amdgpu_buffer_rsrc_t r, uint8
 // holds K-chunk g * STEPS + t of its weight row (fp4: one 32-element block; bf16: 8
 // elements) and the same chunk of its activation row; FP8 activation rows give each lane
 // the chunks 2t+g and 4+2t+g that the FP8 operand layout pairs with those FP4 blocks.
-template <int MODE>
+//
+// `after(k)` runs after the k-th read (k = 0 .. 7, or 11 for W4A8).  LDS-DMA loads issued
+// from it land in program order between the reads: the compiler cannot move a read past a
+// DMA that may write the same LDS array, so source order is the only way to interleave.
+template <int MODE, class After>
 __device__ __forceinline__ void read_frags(v4i (&f)[12], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
-                                           uint32_t lane, int t) {
+                                           uint32_t lane, int t, After&& after) {
   using F = Fast<MODE>;
   const uint32_t g = lane >> 5, r32 = lane & 31;
   const uint32_t chunk = g * F::STEPS + t;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 4; ++i) {
     f[i] = *reinterpret_cast<const v4i*>(lw + swz<F::W_RB>(wn * 128 + 32 * i + r32, chunk));
+    after(i);
+  }
   if constexpr (MODE == GEMM_W4A8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t row = wm * 128 + 32 * j + r32;
       f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 2 * t + g));
+      after(4 + 2 * j);
       f[8 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 4 + 2 * t + g));
+      after(5 + 2 * j);
     }
   } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) {
       f[4 + j] = *reinterpret_cast<const v4i*>(la + swz<F::A_RB>(wm * 128 + 32 * j + r32, chunk));
+      after(4 + j);
+    }
   }
 }
+
+template <int MODE>
+__device__ __forceinline__ void read_frags(v4i (&f)[12], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
+                                           uint32_t lane, int t) {
+  read_frags<MODE>(f, la, lw, wm, wn, lane, t, [](int) {});
+}
+
+// number of the n DMA loads spread over rd reads that go out right after read k
+constexpr int dma_after(int k, int n, int rd) { return (k + 1) * n / rd - k * n / rd; }
 
 template <int MODE, int T>
 __device__ __forceinline__ void mfma16(v16f (&acc)[4][4], const v4i (&f)[12], const uint32_t (&scw)[4],
@@ -425,19 +444,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   using C = Fast<MODE>;
   constexpr uint32_t A_TILE = BM * C::A_RB;
   constexpr uint32_t W_TILE = BN * C::W_RB;
-  // scale bytes per row per window (4 blocks for both scaled modes, none for bf16)
-  constexpr uint32_t SC_WIN = C::SC_WIN;
-  constexpr uint32_t SW_TILE = BN * SC_WIN;
-  constexpr uint32_t SA_TILE = (MODE == GEMM_W4A4) ? BM * SC_WIN : 0;
-  constexpr uint32_t BUF = A_TILE + W_TILE + SW_TILE + SA_TILE;
+  constexpr uint32_t BUF = A_TILE + W_TILE;    // one tile stage
   constexpr int A_LINES = A_TILE / 1024 / 4;   // 1 KB LDS lines per wave per window
   constexpr int W_LINES = W_TILE / 1024 / 4;
-  constexpr int SW_LINES = SW_TILE / 256 / 4;  // 256-byte lines (4-byte DMA) per wave
-  constexpr int SA_LINES = SA_TILE / 256 / 4;
   constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
   constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
   constexpr int NS = C::NS;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * BUF];
+  // Scales travel in chunks of SC_ROW bytes per row (CW windows) through a two-slot ring
+  // beside the tile stages: a load instruction costs the memory pipeline per cache line
+  // touched, so a few bytes per row per window would cost as much as the tiles themselves.
+  // A slot holds the weight rows' chunk, then (W4A4) the activation rows'.
+  constexpr uint32_t SC_WIN = C::SC_WIN;       // scale bytes per row per window
+  constexpr bool HAS_SC = SC_WIN > 0;
+  constexpr uint32_t SC_ROW = 32;
+  constexpr int CW = HAS_SC ? (int)(SC_ROW / SC_WIN) : 1;
+  constexpr uint32_t SC_ROWS = HAS_SC ? BN + (MODE == GEMM_W4A4 ? BM : 0) : 0;
+  constexpr uint32_t SLOT = SC_ROWS * SC_ROW;
+  constexpr int SC_LINES = (int)(SLOT / 1024 / 4);   // 1 KB lines (32 rows) per wave per chunk
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * BUF + 2 * SLOT];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
@@ -482,35 +506,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   uint32_t a_voff0, a_voff1, w_voff0, w_voff1;
   dma_voffs(A_CPR, p.a_row_bytes, a_voff0, a_voff1);
   dma_voffs(W_CPR, p.w_row_bytes, w_voff0, w_voff1);
-  // Scale planes are staged per window as [row][SC_WIN bytes] with 4-byte DMA: dword d of
-  // the plane is row d / (SC_WIN/4), word d % (SC_WIN/4).
-  constexpr uint32_t SC_WORDS = SC_WIN / 4 > 0 ? SC_WIN / 4 : 1;
-  const uint32_t sc_voff = (lane / SC_WORDS) * p.scale_row_bytes + (lane % SC_WORDS) * 4;
-  constexpr uint32_t SC_ROWS_PER_LINE = 64 / SC_WORDS;
+  // scale chunk lines: lane i fetches bytes 16 (i & 1) .. + 16 of row i / 2 of the line
+  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
 
-  // A window's loads in two parts, issued under different MFMA steps so that the four
-  // waves never queue a whole window of DMA at once: part 0 = activation tile and its
-  // scales, part 1 = weight tile and its scales.
+  // A window's tile loads in two parts, issued under different MFMA steps so that the
+  // four waves never queue a whole window of DMA at once: part 0 = activation tile,
+  // part 1 = weight tile.
   auto issue_part = [&](int w, uint32_t stage, auto part_tag) {
     constexpr int PART = decltype(part_tag)::value;
     uint8_t* la = lds + stage;
     uint8_t* lw = la + A_TILE;
-    uint8_t* lsw = lw + W_TILE;
-    uint8_t* lsa = lsw + SW_TILE;
     if constexpr (PART == 0) {
 #pragma unroll
       for (int j = 0; j < A_LINES; ++j) {
         const uint32_t line = wave * A_LINES + j;
         load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
                          (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
-      }
-      if constexpr (SA_TILE > 0) {
-#pragma unroll
-        for (int j = 0; j < SA_LINES; ++j) {
-          const uint32_t line = wave * SA_LINES + j;
-          load_dword_to_lds(rsa, lsa + line * 256, sc_voff,
-                            (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
-        }
       }
     } else {
 #pragma unroll
@@ -519,36 +530,59 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
         load_line_to_lds(rw, lw + line * 1024, (line & 1) ? w_voff1 : w_voff0,
                          (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
       }
-      if constexpr (SC_WIN > 0) {
-#pragma unroll
-        for (int j = 0; j < SW_LINES; ++j) {
-          const uint32_t line = wave * SW_LINES + j;
-          load_dword_to_lds(rsw, lsw + line * 256, sc_voff,
-                            (uint32_t)w * SC_WIN + line * SC_ROWS_PER_LINE * p.scale_row_bytes);
-        }
-      }
+    }
+  };
+  // one line of a window's tile: part 0 = activation tile, part 1 = weight tile
+  auto issue_line = [&](int w, uint32_t stage, auto part_tag, int j) {
+    constexpr int PART = decltype(part_tag)::value;
+    uint8_t* la = lds + stage;
+    if constexpr (PART == 0) {
+      const uint32_t line = wave * A_LINES + j;
+      load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+                       (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
+    } else {
+      const uint32_t line = wave * W_LINES + j;
+      load_line_to_lds(rw, la + A_TILE + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+                       (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
     }
   };
   auto issue_loads = [&](int w, uint32_t stage) {
     issue_part(w, stage, std::integral_constant<int, 0>{});
     issue_part(w, stage, std::integral_constant<int, 1>{});
   };
-  // this lane's scale bytes for the window in `stage`: W rows (4 n-fragments), A rows
-  // (4 m-fragments); byte t is the block of MFMA step t (op_sel t)
-  auto read_scales = [&](uint32_t stage, uint32_t (&scw)[4], uint32_t (&sca)[4]) {
-    if constexpr (SC_WIN > 0) {
+  // scale chunk c (windows c*CW ..) into slot c & 1
+  const int nchunks = (p.nwin + CW - 1) / CW;
+  auto issue_chunk = [&](int c) {
+    uint8_t* slot = lds + NS * BUF + (uint32_t)(c & 1) * SLOT;
+#pragma unroll
+    for (int j = 0; j < SC_LINES; ++j) {
+      const uint32_t line = wave * SC_LINES + j;
+      const bool is_w = line < BN / 32;
+      const uint32_t row0 = (is_w ? line : line - BN / 32) * 32;
+      load_line_to_lds(is_w ? rsw : rsa, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
+    }
+  };
+  // Chunk c+1 goes out at the start of window c*CW (c >= 1; chunk 1 in the prologue): the
+  // barrier that ended window c*CW - 1 follows every wave's last read of chunk c-1, the
+  // slot's previous occupant, and issuing ahead of the window's pending tile loads keeps
+  // the chunk older than every tile load the hand-over waits for.
+  auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
+  // this lane's scale bytes for window w: W rows (4 n-fragments), A rows (4 m-fragments);
+  // byte t is the block of MFMA step t (op_sel t)
+  auto read_scales = [&](int w, uint32_t (&scw)[4], uint32_t (&sca)[4]) {
+    if constexpr (HAS_SC) {
       // lane group g's blocks g*STEPS .. g*STEPS+STEPS-1 as bytes 0.. of one word
-      const uint8_t* lsw = lds + stage + A_TILE + W_TILE;
+      const uint8_t* slot = lds + NS * BUF + (uint32_t)((w / CW) & 1) * SLOT;
       const uint32_t g = lane >> 5, r32 = lane & 31;
-      const uint32_t word = (SC_WIN == 8) ? 4 * g : 0, sh = (SC_WIN == 8) ? 0 : 16 * g;
+      const uint32_t col = (uint32_t)(w % CW) * SC_WIN + ((SC_WIN == 8) ? 4 * g : 0);
+      const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * g;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        scw[i] = *reinterpret_cast<const uint32_t*>(lsw + (wn * 128 + 32 * i + r32) * SC_WIN + word) >> sh;
-      if constexpr (SA_TILE > 0) {
-        const uint8_t* lsa = lsw + SW_TILE;
+        scw[i] = *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i + r32) * SC_ROW + col) >> sh;
+      if constexpr (MODE == GEMM_W4A4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sca[j] = *reinterpret_cast<const uint32_t*>(lsa + (wm * 128 + 32 * j + r32) * SC_WIN + word) >> sh;
+          sca[j] = *reinterpret_cast<const uint32_t*>(slot + (BN + wm * 128 + 32 * j + r32) * SC_ROW + col) >> sh;
       }
     }
   };
@@ -565,15 +599,18 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   uint32_t scw[4] = {0, 0, 0, 0}, sca[4] = {0, 0, 0, 0};
   v4i f0[12], f1[12];
   constexpr int RD = (MODE == GEMM_W4A8) ? 12 : 8;       // ds_read_b128 per fragment set
-  constexpr int VM = A_LINES + W_LINES + SW_LINES + SA_LINES;   // LDS-DMA loads per wave per window
-  constexpr int VM0 = A_LINES + SA_LINES, VM1 = W_LINES + SW_LINES;  // per part
-  constexpr int SR = (MODE == GEMM_W4A4) ? 8 : (MODE == GEMM_W4A8 ? 4 : 0);   // scale reads
+  constexpr int VM = A_LINES + W_LINES;                  // tile DMA loads per wave per window
+  constexpr int VM0 = A_LINES, VM1 = W_LINES;            // per part
 
-  // prologue: window k goes to stage k % NS.  Window 0 resident, windows 1 .. NS-1 in
-  // flight, step-0 fragments and scales read.
+  // prologue: window k goes to stage k % NS.  Window 0 and scale chunk 0 resident, chunk 1
+  // and windows 1 .. NS-1 in flight (the chunk first, so the hand-over wait counts below
+  // see only tile loads after it), step-0 fragments and scales read.
   issue_loads(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);          // vmcnt/lgkmcnt = 0: stage 0 written
+  if constexpr (HAS_SC) issue_chunk(0);
+  __builtin_amdgcn_s_waitcnt(0);          // vmcnt/lgkmcnt = 0: stage 0 and chunk 0 written
   __syncthreads();
+  if constexpr (HAS_SC)
+    if (nchunks > 1) issue_chunk(1);
 #pragma unroll
   for (int k = 1; k < NS; ++k)
     if (k < nwin) issue_loads(k, k * BUF);
@@ -584,8 +621,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // and, once every wave is past stage `cur`, refills it with part 0 of window w+NS.
   // PEND: part 1 of window w+NS-1 (whose part 0 went out after the previous barrier) is
   // issued under this window's step-0 MFMAs.  The tail (last NS windows) waits for
-  // everything and loads nothing.  No control flow inside, so nothing can be sunk past the
-  // barrier.
+  // everything and loads no tiles.  Memory-free MFMAs cannot be sunk past the barrier:
+  // every step is its own scheduling region.
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
   auto window = [&](int w, auto pend_tag, auto steady_tag) {
     constexpr bool PEND = decltype(pend_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
@@ -593,43 +632,63 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     const uint32_t nxt_stage = (uint32_t)((w + 1) % NS) * BUF;
     const uint8_t* la = lds + cur;
     const uint8_t* lw = la + A_TILE;
-    if constexpr (PEND) issue_part(w + NS - 1, (uint32_t)((w + NS - 1) % NS) * BUF, std::integral_constant<int, 1>{});
-    // steps 0 .. STEPS-2: the next step's fragments are read under this step's MFMAs
+    if constexpr (HAS_SC)
+      if (chunk_due(w)) issue_chunk(w / CW + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint32_t last_stage = (uint32_t)((w + NS - 1) % NS) * BUF;
+    // part 1 of window w+NS-1, spread over the reads of step 0
+    auto pend_loads = [&](int k) {
+      if constexpr (PEND)
+        if (dma_after(k, VM1, RD) > 0) issue_line(w + NS - 1, last_stage, I1{}, k * VM1 / RD);
+    };
+    // Steps 0 .. STEPS-2, one scheduling region each (a region boundary after every step
+    // keeps the compiler from mixing steps, which reuses fragment registers early and
+    // forces waits on reads just issued): the next step's fragments are read under this
+    // step's 16 MFMAs.  Step 0 also carries the pending weight-tile loads, at most one per
+    // two MFMAs so that the four waves together stay within the rate the vector memory
+    // pipeline accepts (a full queue stalls the wave, and with it the matrix core).  The
+    // next window's scales are read a region early: their chunk is resident and visible
+    // at least one hand-over before (CW >= 3), so the copy after the hand-over never waits.
+    uint32_t scw_n[4], sca_n[4];
     if constexpr (C::STEPS == 4) {
-      read_frags<MODE>(f1, la, lw, wm, wn, lane, 1);
+      read_frags<MODE>(f1, la, lw, wm, wn, lane, 1, pend_loads);
       mfma16<MODE, 0>(acc, f0, scw, sca);
-      read_frags<MODE>(f0, la, lw, wm, wn, lane, 2);
-      mfma16<MODE, 1>(acc, f1, scw, sca);
-      read_frags<MODE>(f1, la, lw, wm, wn, lane, 3);
-      mfma16<MODE, 2>(acc, f0, scw, sca);
-      // step 0: its 16 MFMAs cover the next step's reads and the pending loads
 #pragma unroll
-      for (int r = 0; r < RD; ++r) {
+      for (int r = 0; r < 8; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // 1 DS read
-        if (PEND && r < VM1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
+        if (PEND && dma_after(r, VM1, RD) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // 1 VMEM
         __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);      // 2 MFMA
       }
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags<MODE>(f0, la, lw, wm, wn, lane, 2);
+      read_scales(w + 1, scw_n, sca_n);
+      mfma16<MODE, 1>(acc, f1, scw, sca);
 #pragma unroll
-      for (int k = 1; k < 3; ++k)
-#pragma unroll
-        for (int r = 0; r < RD; ++r) {
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-        }
-    } else {
-      read_frags<MODE>(f1, la, lw, wm, wn, lane, 1);
-      mfma16<MODE, 0>(acc, f0, scw, sca);
-#pragma unroll
-      for (int r = 0; r < RD; ++r) {
+      for (int r = 0; r < 16; ++r) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        if (PEND && r < VM1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
       }
-      __builtin_amdgcn_sched_group_barrier(0x008, 16 - RD, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags<MODE>(f1, la, lw, wm, wn, lane, 3);
+      mfma16<MODE, 2>(acc, f0, scw, sca);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      }
+    } else {
+      read_frags<MODE>(f1, la, lw, wm, wn, lane, 1, pend_loads);
+      read_scales(w + 1, scw_n, sca_n);
+      mfma16<MODE, 0>(acc, f0, scw, sca);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if (PEND && r < RD && dma_after(r, VM1, RD) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      }
     }
     // Hand-over, kept on this side of the last step's MFMAs (which touch no memory and
     // would otherwise be moved below the barrier, exposing the LDS reads).
-    uint32_t scw_n[4], sca_n[4];
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (STEADY && NS > 2)
       __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * VM));   // window w+1 landed
@@ -637,24 +696,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
       __builtin_amdgcn_s_waitcnt(0);
     stage_barrier();                      // every wave is past stage `cur`
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (STEADY) issue_part(w + NS, cur, std::integral_constant<int, 0>{});
-    read_frags<MODE>(f0, lds + nxt_stage, lds + nxt_stage + A_TILE, wm, wn, lane, 0);
-    read_scales(nxt_stage, scw_n, sca_n);
+    // part 0 of window w+NS into the stage just released, spread over the next window's
+    // step-0 reads
+    read_frags<MODE>(f0, lds + nxt_stage, lds + nxt_stage + A_TILE, wm, wn, lane, 0, [&](int k) {
+      if constexpr (STEADY)
+        if (dma_after(k, VM0, RD) > 0) issue_line(w + NS, cur, I0{}, k * VM0 / RD);
+    });
     if constexpr (C::STEPS == 4)
       mfma16<MODE, 3>(acc, f1, scw, sca);
     else
       mfma16<MODE, 1>(acc, f1, scw, sca);
-    if constexpr (STEADY) {
+    constexpr int MPR = 16 / RD > 1 ? 2 : 1;   // MFMAs per read slot (16 / RD rounded down, at most 2)
 #pragma unroll
-      for (int k = 0; k < VM0; ++k) {
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // 1 VMEM (LDS-DMA) load
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);   // 1 MFMA
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < RD + SR; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+    for (int r = 0; r < 16 / MPR; ++r) {
+      if (r < RD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);                               // DS read
+      if (STEADY && r < RD && dma_after(r, VM0, RD) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 1);   // VMEM
+      __builtin_amdgcn_sched_group_barrier(0x008, MPR, 1);                                         // MFMA
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -728,14 +785,16 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
   p.M = (int)M;
   p.N = (int)N;
   p.scale_row_bytes = (uint32_t)(K / 32);
-  p.scale_dword_ok = (K / 32) % 4 == 0 ? 1 : 0;
+  auto aligned_to = [](const void* q, uintptr_t a) { return (reinterpret_cast<uintptr_t>(q) % a) == 0; };
+  p.scale_dword_ok = ((K / 32) % 4 == 0 && aligned_to(a_scales, 4) && aligned_to(w_scales, 4)) ? 1 : 0;
   p.a_scale = a_scale;
   p.vec_store = (ld_out % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0) ? 1 : 0;
   p.tiles_m = (int)((M + BM - 1) / BM);
   p.tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(NT);
-  // the fast path needs whole windows (and, with scales, 4-byte scale rows)
-  const bool scales_ok = (K / 32) % 4 == 0;
+  // the fast path needs whole windows and, with scales, scale rows and planes on 16-byte
+  // boundaries (they are fetched 16 bytes per lane)
+  const bool scales_ok = (K / 32) % 16 == 0 && aligned_to(a_scales, 16) && aligned_to(w_scales, 16);
   auto launch = [&](auto mode_tag, uint32_t a_row_bytes, uint32_t w_row_bytes, bool needs_scales) {
     constexpr int MD = decltype(mode_tag)::value;
     p.a_row_bytes = a_row_bytes;
