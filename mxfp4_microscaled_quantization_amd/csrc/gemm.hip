@@ -93,7 +93,8 @@ struct Params {
   uint32_t a_row_bytes, w_row_bytes, scale_row_bytes;
   int nwin, tiles_m, tiles_n;
   float a_scale;
-  int vec_store;
+  int vec_store;   // 8-byte output stores allowed (pitch and base)
+  int vec16;       // 16-byte output stores allowed
   int scale_dword_ok;
 };
 
@@ -731,8 +732,47 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   }
   for (; w < nwin; ++w) window(w, F_{}, F_{});
 
-  // ---- epilogue: fp32 -> bf16 (RNE); a lane owns 4 consecutive columns per store ----
+  // ---- epilogue: fp32 -> bf16 (RNE) ----
   const uint32_t r32 = lane & 31, g = lane >> 5;
+  if (p.vec16 && n0 + BN <= p.N) {
+    // A lane holds 4 consecutive columns of 32 different rows, so a direct store touches
+    // 32 cache lines per instruction.  Each wave instead parks its 128 x 128 sub-tile in
+    // its own 32 KB of LDS (16-byte chunk c of row r at slot c ^ (r & 15), spreading the
+    // writes of 16 rows over all banks) and stores 4 whole 256-byte row segments per
+    // instruction.  After the last hand-over barrier no wave reads tile data from LDS.
+    __syncthreads();
+    uint8_t* sub = lds + wave * (128u * 256u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = 32 * j + r32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+          float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+          if constexpr (MODE == GEMM_W4A8) {
+            v0 *= p.a_scale;
+            v1 *= p.a_scale;
+            v2 *= p.a_scale;
+            v3 *= p.a_scale;
+          }
+          const uint32_t chunk = 4 * i + pp;
+          *reinterpret_cast<v2u*>(sub + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * g) =
+              v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+    }
+    const int mw = m0 + (int)wm * 128;
+    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
+      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
+      if (mw + (int)row < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)row * p.ld_out + c * 8) = v;
+    }
+    return;
+  }
+  // partial column tiles: a lane owns 4 consecutive columns per store
   const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -789,6 +829,7 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
   p.scale_dword_ok = ((K / 32) % 4 == 0 && aligned_to(a_scales, 4) && aligned_to(w_scales, 4)) ? 1 : 0;
   p.a_scale = a_scale;
   p.vec_store = (ld_out % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0) ? 1 : 0;
+  p.vec16 = (ld_out % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) ? 1 : 0;
   p.tiles_m = (int)((M + BM - 1) / BM);
   p.tiles_n = (int)((N + BN - 1) / BN);
   const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(NT);
