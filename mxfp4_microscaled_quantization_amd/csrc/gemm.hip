@@ -54,19 +54,20 @@ template <> struct Cfg<GEMM_BF16> {
 };
 
 // Fast-path geometry.  A_RB / W_RB: bytes per row per K-window for the activation / weight
-// tile (128 bytes: whole cache lines per row); STEPS: 32x32 MFMA steps per window; NS: LDS
-// stages (a window's loads get NS-1 windows of compute to land); SC_WIN: scale bytes per row
+// tile (128 bytes: whole cache lines per row); STEPS: 32x32 MFMA steps per window; NA / NW:
+// depth of the activation / weight tile rings in LDS (a window's loads get about NA-1
+// windows of compute to land); SC_WIN: scale bytes per row
 // per window.  Lane group g at step t holds K-chunk g * STEPS + t of the weight row (and of
 // the activation row for FP4 / bf16 activations).
 template <int MODE> struct Fast;
 template <> struct Fast<GEMM_W4A4> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NS = 2, SC_WIN = 8;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NA = 2, NW = 2, SC_WIN = 8;
 };
 template <> struct Fast<GEMM_W4A8> {
-  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NS = 3, SC_WIN = 4;
+  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NA = 3, NW = 3, SC_WIN = 4;
 };
 template <> struct Fast<GEMM_BF16> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NS = 2, SC_WIN = 0;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NA = 3, NW = 2, SC_WIN = 0;
 };
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= 0, expcnt unconstrained
@@ -450,7 +451,17 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   constexpr int W_LINES = W_TILE / 1024 / 4;
   constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
   constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
-  constexpr int NS = C::NS;
+  constexpr int NA = C::NA, NW = C::NW;
+  // Equal rings: window w+N's activation tile goes out at the hand-over of window w into
+  // the slot it releases, its weight tile under the next window's step 0.  Deeper
+  // activation ring (the bf16 reference, whose activations stream from HBM while the
+  // weights stay in the last-level caches): the weight tile of window w+NW goes out at the
+  // hand-over, the activation tile of window w+NA-1 under step 0 of window w, so
+  // activations get about two windows to land and weights one.
+  constexpr bool SPLIT = NA != NW;
+  static_assert(!SPLIT || (NA == 3 && NW == 2), "split rings: three activation, two weight slots");
+  constexpr int NS = NA;                       // windows issued ahead by the prologue + 1
+  constexpr uint32_t W_BASE = NA * A_TILE, SC_BASE = NA * A_TILE + NW * W_TILE;
   // Scales travel in chunks of SC_ROW bytes per row (CW windows) through a two-slot ring
   // beside the tile stages: a load instruction costs the memory pipeline per cache line
   // touched, so a few bytes per row per window would cost as much as the tiles themselves.
@@ -462,7 +473,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   constexpr uint32_t SC_ROWS = HAS_SC ? BN + (MODE == GEMM_W4A4 ? BM : 0) : 0;
   constexpr uint32_t SLOT = SC_ROWS * SC_ROW;
   constexpr int SC_LINES = (int)(SLOT / 1024 / 4);   // 1 KB lines (32 rows) per wave per chunk
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * BUF + 2 * SLOT];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[SC_BASE + 2 * SLOT];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
@@ -513,48 +524,32 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // A window's tile loads in two parts, issued under different MFMA steps so that the
   // four waves never queue a whole window of DMA at once: part 0 = activation tile,
   // part 1 = weight tile.
-  auto issue_part = [&](int w, uint32_t stage, auto part_tag) {
+  // ring slots of window w's tiles
+  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NA) * A_TILE; };
+  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NW) * W_TILE; };
+  // one line of window w's tile: part 0 = activation tile, part 1 = weight tile
+  auto issue_line = [&](int w, auto part_tag, int j) {
     constexpr int PART = decltype(part_tag)::value;
-    uint8_t* la = lds + stage;
-    uint8_t* lw = la + A_TILE;
-    if constexpr (PART == 0) {
-#pragma unroll
-      for (int j = 0; j < A_LINES; ++j) {
-        const uint32_t line = wave * A_LINES + j;
-        load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
-                         (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
-      }
-    } else {
-#pragma unroll
-      for (int j = 0; j < W_LINES; ++j) {
-        const uint32_t line = wave * W_LINES + j;
-        load_line_to_lds(rw, lw + line * 1024, (line & 1) ? w_voff1 : w_voff0,
-                         (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
-      }
-    }
-  };
-  // one line of a window's tile: part 0 = activation tile, part 1 = weight tile
-  auto issue_line = [&](int w, uint32_t stage, auto part_tag, int j) {
-    constexpr int PART = decltype(part_tag)::value;
-    uint8_t* la = lds + stage;
     if constexpr (PART == 0) {
       const uint32_t line = wave * A_LINES + j;
-      load_line_to_lds(ra, la + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+      load_line_to_lds(ra, a_slot(w) + line * 1024, (line & 1) ? a_voff1 : a_voff0,
                        (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
     } else {
       const uint32_t line = wave * W_LINES + j;
-      load_line_to_lds(rw, la + A_TILE + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+      load_line_to_lds(rw, w_slot(w) + line * 1024, (line & 1) ? w_voff1 : w_voff0,
                        (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
     }
   };
-  auto issue_loads = [&](int w, uint32_t stage) {
-    issue_part(w, stage, std::integral_constant<int, 0>{});
-    issue_part(w, stage, std::integral_constant<int, 1>{});
+  auto issue_loads = [&](int w) {
+#pragma unroll
+    for (int j = 0; j < A_LINES; ++j) issue_line(w, std::integral_constant<int, 0>{}, j);
+#pragma unroll
+    for (int j = 0; j < W_LINES; ++j) issue_line(w, std::integral_constant<int, 1>{}, j);
   };
   // scale chunk c (windows c*CW ..) into slot c & 1
   const int nchunks = (p.nwin + CW - 1) / CW;
   auto issue_chunk = [&](int c) {
-    uint8_t* slot = lds + NS * BUF + (uint32_t)(c & 1) * SLOT;
+    uint8_t* slot = lds + SC_BASE + (uint32_t)(c & 1) * SLOT;
 #pragma unroll
     for (int j = 0; j < SC_LINES; ++j) {
       const uint32_t line = wave * SC_LINES + j;
@@ -573,7 +568,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   auto read_scales = [&](int w, uint32_t (&scw)[4], uint32_t (&sca)[4]) {
     if constexpr (HAS_SC) {
       // lane group g's blocks g*STEPS .. g*STEPS+STEPS-1 as bytes 0.. of one word
-      const uint8_t* slot = lds + NS * BUF + (uint32_t)((w / CW) & 1) * SLOT;
+      const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
       const uint32_t g = lane >> 5, r32 = lane & 31;
       const uint32_t col = (uint32_t)(w % CW) * SC_WIN + ((SC_WIN == 8) ? 4 * g : 0);
       const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * g;
@@ -601,46 +596,53 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   v4i f0[12], f1[12];
   constexpr int RD = (MODE == GEMM_W4A8) ? 12 : 8;       // ds_read_b128 per fragment set
   constexpr int VM = A_LINES + W_LINES;                  // tile DMA loads per wave per window
-  constexpr int VM0 = A_LINES, VM1 = W_LINES;            // per part
+  // tile loads issued under step 0 (VM1) and at the hand-over (VM0)
+  constexpr int VM1 = SPLIT ? A_LINES : W_LINES, VM0 = SPLIT ? W_LINES : A_LINES;
+  // loads allowed in flight when the hand-over has to see window w+1 complete
+  constexpr int WAIT_VM = SPLIT ? A_LINES : (NA - 2) * VM;
 
-  // prologue: window k goes to stage k % NS.  Window 0 and scale chunk 0 resident, chunk 1
-  // and windows 1 .. NS-1 in flight (the chunk first, so the hand-over wait counts below
-  // see only tile loads after it), step-0 fragments and scales read.
-  issue_loads(0, 0);
+  // prologue: window 0 and scale chunk 0 resident, chunk 1 and windows 1 .. NS-1 in flight
+  // (the chunk first, so the hand-over wait counts below see only tile loads after it),
+  // step-0 fragments and scales read.
+  issue_loads(0);
   if constexpr (HAS_SC) issue_chunk(0);
   __builtin_amdgcn_s_waitcnt(0);          // vmcnt/lgkmcnt = 0: stage 0 and chunk 0 written
   __syncthreads();
   if constexpr (HAS_SC)
     if (nchunks > 1) issue_chunk(1);
 #pragma unroll
-  for (int k = 1; k < NS; ++k)
-    if (k < nwin) issue_loads(k, k * BUF);
-  read_frags<MODE>(f0, lds, lds + A_TILE, wm, wn, lane, 0);
+  for (int k = 1; k < (SPLIT ? 2 : NS); ++k)
+    if (k < nwin) issue_loads(k);
+  read_frags<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
   read_scales(0, scw, sca);
 
-  // One window.  STEADY: windows w+1 .. w+NS exist; the hand-over waits for window w+1 only
-  // and, once every wave is past stage `cur`, refills it with part 0 of window w+NS.
-  // PEND: part 1 of window w+NS-1 (whose part 0 went out after the previous barrier) is
-  // issued under this window's step-0 MFMAs.  The tail (last NS windows) waits for
-  // everything and loads no tiles.  Memory-free MFMAs cannot be sunk past the barrier:
-  // every step is its own scheduling region.
+  // One window.  PEND: the step-0 tile loads go out (equal rings: the weight tile of window
+  // w+NS-1, whose activation tile went out at the previous hand-over; split rings: the
+  // activation tile of window w+NA-1).  STEADY: the hand-over waits for window w+1 only
+  // and refills the slot(s) this window releases (equal rings: activation tile of window
+  // w+NS; split rings: weight tile of window w+NW).  The tail waits for everything and
+  // loads no tiles.  Memory-free MFMAs cannot be sunk past the barrier: every step is its
+  // own scheduling region.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto window = [&](int w, auto pend_tag, auto steady_tag) {
     constexpr bool PEND = decltype(pend_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
-    const uint32_t cur = (uint32_t)(w % NS) * BUF;
-    const uint32_t nxt_stage = (uint32_t)((w + 1) % NS) * BUF;
-    const uint8_t* la = lds + cur;
-    const uint8_t* lw = la + A_TILE;
+    const uint8_t* la = a_slot(w);
+    const uint8_t* lw = w_slot(w);
     if constexpr (HAS_SC)
       if (chunk_due(w)) issue_chunk(w / CW + 1);
     __builtin_amdgcn_sched_barrier(0);
-    const uint32_t last_stage = (uint32_t)((w + NS - 1) % NS) * BUF;
-    // part 1 of window w+NS-1, spread over the reads of step 0
+    // step-0 tile loads, spread over the reads of step 0
     auto pend_loads = [&](int k) {
-      if constexpr (PEND)
-        if (dma_after(k, VM1, RD) > 0) issue_line(w + NS - 1, last_stage, I1{}, k * VM1 / RD);
+      if constexpr (PEND) {
+        if (dma_after(k, VM1, RD) > 0) {
+          if constexpr (SPLIT)
+            issue_line(w + NA - 1, I0{}, k * VM1 / RD);
+          else
+            issue_line(w + NS - 1, I1{}, k * VM1 / RD);
+        }
+      }
     };
     // Steps 0 .. STEPS-2, one scheduling region each (a region boundary after every step
     // keeps the compiler from mixing steps, which reuses fragment registers early and
@@ -691,17 +693,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     // Hand-over, kept on this side of the last step's MFMAs (which touch no memory and
     // would otherwise be moved below the barrier, exposing the LDS reads).
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (STEADY && NS > 2)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm((NS - 2) * VM));   // window w+1 landed
+    if constexpr (STEADY && WAIT_VM > 0)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_VM));   // window w+1 landed
     else
       __builtin_amdgcn_s_waitcnt(0);
     stage_barrier();                      // every wave is past stage `cur`
     __builtin_amdgcn_sched_barrier(0);
-    // part 0 of window w+NS into the stage just released, spread over the next window's
-    // step-0 reads
-    read_frags<MODE>(f0, lds + nxt_stage, lds + nxt_stage + A_TILE, wm, wn, lane, 0, [&](int k) {
-      if constexpr (STEADY)
-        if (dma_after(k, VM0, RD) > 0) issue_line(w + NS, cur, I0{}, k * VM0 / RD);
+    // refill the slot just released, spread over the next window's step-0 reads
+    read_frags<MODE>(f0, a_slot(w + 1), w_slot(w + 1), wm, wn, lane, 0, [&](int k) {
+      if constexpr (STEADY) {
+        if (dma_after(k, VM0, RD) > 0) {
+          if constexpr (SPLIT)
+            issue_line(w + NW, I1{}, k * VM0 / RD);
+          else
+            issue_line(w + NS, I0{}, k * VM0 / RD);
+        }
+      }
     });
     if constexpr (C::STEPS == 4)
       mfma16<MODE, 3>(acc, f1, scw, sca);
@@ -724,7 +731,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   using T_ = std::true_type;
   using F_ = std::false_type;
   int w = 0;
-  if (nwin > NS) {
+  if constexpr (SPLIT) {
+    // windows 0 and 1 come from the prologue; window w loads tiles of window w+2
+    for (; w < nwin - 2; ++w) window(w, T_{}, T_{});
+  } else if (nwin > NS) {
     window(0, F_{}, T_{});
     for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{});
     window(w, T_{}, F_{});
