@@ -42,7 +42,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="wan_ffn_down_sqnr")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-rows", type=int, default=4096, help="activation rows in the CPU oracle sample")
+    p.add_argument("--cpu-rows", type=int, default=6144, help="activation rows in the CPU oracle sample")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for HBM counter scaling)")
     return p.parse_args()
