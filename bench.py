@@ -226,6 +226,33 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
 
+    # ---- outside the timed step: the UOS scale rule (quantize rate, W4A4 SQNR on the same
+    # workload, both operands quantized with UOS) ----
+    def time_fn(fn, n=10):
+        fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(n):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    ms_uos = time_fn(lambda: mxq.quantize_into(a, ac, asc, rule="uos"))
+    wc_u, wsc_u = mxq.quantize(w, rule="uos")
+    mxq.quantize_into(a, ac, asc, rule="uos")
+    mxq.gemm_w4a4(ac, asc, wc_u, wsc_u, out=o44)
+    r_u = mxq.sqnr(ref, o44, workspace=ws1)
+    q_amount = work["mxq_quantize"][0]
+    res["next"] = {
+        "uos_scale_rule": {
+            "mxq_quantize_uos": {"ms": round(ms_uos, 4), "achieved": round(q_amount / (ms_uos * 1e-3) / 1e9, 2),
+                                 "unit": "GB/s", "peak": PEAK["hbm_GBps"],
+                                 "frac": round(q_amount / (ms_uos * 1e-3) / 1e9 / PEAK["hbm_GBps"], 4)},
+            "sqnr_db_w4a4": {"ocp": round(float(r44[2].item()), 4), "uos": round(float(r_u[2].item()), 4)},
+        }
+    }
+
     if not args.no_cpu_baseline:
         rows = min(args.cpu_rows, M)
         a_rows = a[:rows]

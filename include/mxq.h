@@ -85,6 +85,25 @@ mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
                         uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                         void* stream);
 
+/* Scale rule of mxq_quantize_rule. */
+typedef enum {
+  MXQ_SCALE_OCP = 0, /* X = 2^(floor(log2 amax) - 2): the rule of mxq_quantize */
+  MXQ_SCALE_UOS = 1  /* X = smallest power of two with amax <= 7.25 X */
+} mxq_scale_rule;
+
+/*
+ * mxq_quantize_rule -- mxq_quantize with a choice of block scale rule.
+ * MXQ_SCALE_UOS follows [MXA] "What it actually does" (Universal Optimal Scaling, a
+ * data-free scaling boundary Qmax = 7.25): X = 2^k with k the smallest integer such that
+ * amax <= 7.25 * 2^k, clamped to [-127, 127]; all-zero block -> 0x00.  Equivalently the
+ * OCP byte plus one when the significand of amax exceeds 1.8125, floored at 0.  The
+ * element rounding, layout, arguments and errors are those of mxq_quantize; an unknown
+ * rule -> MXQ_ERR_UNSUPPORTED.
+ */
+mxq_status mxq_quantize_rule(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                             uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                             mxq_scale_rule rule, void* stream);
+
 /*
  * mxq_quantize_fp8 -- static FP8 E4M3 activation quantization for W4A8 ([Q13]).
  *   q = E4M3(fl32(x * inv_scale)): one binary32 multiply (round to nearest even), then

@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "lib", "MxqError", "quantize", "quantize_fp8", "absmax", "fp8_static_scales",
+    "lib", "MxqError", "quantize", "quantize_into", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
     "gemm_w4a4", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_workspace_bytes", "dequantize",
     "LIB_PATH", "ABI_SYMBOLS",
 ]
@@ -33,6 +33,8 @@ _i64, _ptr, _f32, _sz = ctypes.c_int64, ctypes.c_void_p, ctypes.c_float, ctypes.
 #: every exported symbol with (restype, argtypes) -- the C ABI of include/mxq.h
 ABI_SYMBOLS = {
     "mxq_quantize": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr]),
+    "mxq_quantize_rule": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, ctypes.c_int,
+                                         _ptr]),
     "mxq_quantize_fp8": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _f32, _ptr, _i64, _ptr]),
     "mxq_absmax": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _ptr]),
     "mxq_gemm_w4a4": (ctypes.c_int, [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
@@ -104,27 +106,38 @@ def _p(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
-def quantize(x: torch.Tensor):
+SCALE_RULES = {"ocp": 0, "uos": 1}
+
+
+def _rule_code(rule: str) -> int:
+    if rule not in SCALE_RULES:
+        raise ValueError(f"scale rule must be one of {sorted(SCALE_RULES)}")
+    return SCALE_RULES[rule]
+
+
+def quantize(x: torch.Tensor, rule: str = "ocp"):
     """MXFP4-quantize rows of ``x`` (bf16 or fp32, [R, K], K % 32 == 0).
 
-    Returns (codes uint8 [R, K/2], scales uint8 [R, K/32]).
+    ``rule``: "ocp" (X = 2^(floor(log2 amax) - 2)) or "uos" (smallest power of two with
+    amax <= 7.25 X).  Returns (codes uint8 [R, K/2], scales uint8 [R, K/32]).
     """
     _dev(x, "x")
     ld = _rowmajor(x, "x")
     R, K = x.shape
     codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
     scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
-    _check(lib.mxq_quantize(_p(x), _dtype_code(x), R, K, ld, _p(codes), K // 2, _p(scales), K // 32, _stream()))
+    _check(lib.mxq_quantize_rule(_p(x), _dtype_code(x), R, K, ld, _p(codes), K // 2, _p(scales), K // 32,
+                                 _rule_code(rule), _stream()))
     return codes, scales
 
 
-def quantize_into(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor):
+def quantize_into(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, rule: str = "ocp"):
     """MXFP4-quantize into caller-provided outputs (may be row-strided views)."""
     _dev(x, "x")
     ld = _rowmajor(x, "x")
     R, K = x.shape
-    _check(lib.mxq_quantize(_p(x), _dtype_code(x), R, K, ld, _p(codes), _rowmajor(codes, "codes"),
-                            _p(scales), _rowmajor(scales, "scales"), _stream()))
+    _check(lib.mxq_quantize_rule(_p(x), _dtype_code(x), R, K, ld, _p(codes), _rowmajor(codes, "codes"),
+                                 _p(scales), _rowmajor(scales, "scales"), _rule_code(rule), _stream()))
 
 
 def fp8_static_scales(amax: float):

@@ -100,9 +100,11 @@ int mxq_abi_version(void) { return MXQ_ABI_VERSION; }
 
 const char* mxq_last_error(void) { return g_error.c_str(); }
 
-mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
-                        int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
+mxq_status mxq_quantize_rule(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                             int64_t ld_codes, uint8_t* scales, int64_t ld_scales, mxq_scale_rule rule, void* stream) {
   const char* fn = "mxq_quantize";
+  if (rule != MXQ_SCALE_OCP && rule != MXQ_SCALE_UOS)
+    return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown scale rule %d", fn, (int)rule);
   mxq_status st = check_input(fn, x, dt, rows, cols, ld_x, 32);
   if (st != MXQ_OK) return st;
   if (ld_codes < cols / 2) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_codes (%lld) < cols/2", fn, (long long)ld_codes);
@@ -113,7 +115,12 @@ mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
       return fail(MXQ_ERR_INVALID_ARG, "%s: codes base and ld_codes must be multiples of 16 bytes", fn);
   }
   return hip_status(fn, mxq::launch_quantize_mxfp4(x, dt == MXQ_F32, rows, cols, ld_x, codes, ld_codes, scales,
-                                                   ld_scales, as_stream(stream)));
+                                                   ld_scales, rule == MXQ_SCALE_UOS, as_stream(stream)));
+}
+
+mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, uint8_t* codes,
+                        int64_t ld_codes, uint8_t* scales, int64_t ld_scales, void* stream) {
+  return mxq_quantize_rule(x, dt, rows, cols, ld_x, codes, ld_codes, scales, ld_scales, MXQ_SCALE_OCP, stream);
 }
 
 mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, float inv_scale,

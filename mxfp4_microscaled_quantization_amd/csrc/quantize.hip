@@ -8,6 +8,12 @@
 // X = 2^(floor(log2 amax) - 2) clamped at 2^-127, and every element becomes the E2M1
 // value nearest to x / X (ties to even, saturating at +-6).
 //
+// UOS variant ("MXAttention ...", section "What it actually does": a data-free scaling
+// boundary Qmax = 7.25): X is the smallest power of two with amax <= 7.25 X.  With
+// amax = m 2^e, m in [1, 2), that is 2^(e-2) when 4m <= 7.25 and 2^(e-1) otherwise, so
+// the byte is the OCP byte plus one exactly when the significand of amax exceeds 1.8125
+// (fraction field above 0x680000 in binary32, 0x68 in bf16), floored at 0 as before.
+//
 // Mapping: four consecutive lanes own one 32-element block (8 elements, 16 bytes of
 // bf16, per lane), so each wave load instruction moves 1 KB of contiguous input and the
 // block maximum is a 2-step DPP reduction inside the quad.  The E2M1 rounding is the
@@ -32,9 +38,15 @@ __device__ __forceinline__ unsigned scale_byte_from_exp(unsigned e) {
   return e == 255u ? 255u : (e > 2u ? e - 2u : 0u);
 }
 
+// UOS: one more when the significand of a normal amax exceeds 1.8125 (bump = 1)
+__device__ __forceinline__ unsigned scale_byte_uos(unsigned e, unsigned bump) {
+  const unsigned t = e + (e != 0u ? bump : 0u);
+  return e == 255u ? 255u : (t > 2u ? t - 2u : 0u);
+}
+
 // ---------------------------------------------------------------------------------
-// MXFP4 quantization.  F32 selects binary32 input (else bf16).
-template <bool F32>
+// MXFP4 quantization.  F32 selects binary32 input (else bf16); UOS the 7.25 boundary.
+template <bool F32, bool UOS>
 __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     const void* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ codes, int64_t ld_codes,
     uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks,
@@ -77,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      unsigned amax, e;
+      unsigned amax, e, bump;
       if (F32) {
         unsigned m = 0;
 #pragma unroll
@@ -87,6 +99,7 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
         }
         amax = quad_max_u32(m);
         e = amax >> 23;
+        bump = (amax & 0x7FFFFFu) > 0x680000u ? 1u : 0u;
       } else {
         v2h m = {0, 0};
 #pragma unroll
@@ -94,8 +107,9 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
           m = __builtin_elementwise_max(m, __builtin_bit_cast(v2h, (unsigned)d0[u][i] & 0x7FFF7FFFu));
         amax = quad_max_u32(max((unsigned)m[0], (unsigned)m[1]));
         e = amax >> 7;
+        bump = (amax & 0x7Fu) > 0x68u ? 1u : 0u;
       }
-      const unsigned s = scale_byte_from_exp(e);
+      const unsigned s = UOS ? scale_byte_uos(e, bump) : scale_byte_from_exp(e);
       const float scale = e8m0_to_f32(s);
       unsigned r = 0;
       if (F32) {
@@ -266,18 +280,20 @@ int grid_for(int64_t work_items, int64_t per_block) {
 
 hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
                                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
-                                 hipStream_t stream) {
+                                 bool uos, hipStream_t stream) {
   const int64_t bpr = cols / 32;
   const int64_t total = rows * bpr;
   if (total == 0) return hipSuccess;
   const int contiguous = (ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr) ? 1 : 0;
   const int grid = grid_for(total, kBlocksPerIter);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes, ld_codes, scales, ld_scales,
+                       (uint32_t)bpr, total, contiguous);
+  };
   if (f32)
-    hipLaunchKernelGGL(mx_quantize_kernel<true>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes,
-                       ld_codes, scales, ld_scales, (uint32_t)bpr, total, contiguous);
+    uos ? go(mx_quantize_kernel<true, true>) : go(mx_quantize_kernel<true, false>);
   else
-    hipLaunchKernelGGL(mx_quantize_kernel<false>, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes,
-                       ld_codes, scales, ld_scales, (uint32_t)bpr, total, contiguous);
+    uos ? go(mx_quantize_kernel<false, true>) : go(mx_quantize_kernel<false, false>);
   return hipGetLastError();
 }
 

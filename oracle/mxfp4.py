@@ -21,6 +21,13 @@ What is computed (pages + the OCP MX rule):
    of a row holds element 2j in the low nibble and 2j+1 in the high nibble.  Scales are
    row-major bytes, one per block.
 
+Optional UOS scale rule ("MXAttention ...", section "What it actually does": Universal
+Optimal Scaling, a data-free scaling boundary Qmax = 7.25).  Reading: the scale is the
+smallest power of two X with amax <= Qmax * X, i.e. the block maximum lands in
+(3.625, 7.25] after scaling and values above 6 but within 7.25 X saturate to 6; the same
+exponent clamp and all-zero rule apply.  The page gives the constant, not the formula;
+this is the plainest reading of "scaling boundary".
+
 Non-finite inputs are outside the contract; the oracle raises on them.
 """
 
@@ -29,6 +36,7 @@ import numpy as np
 from .formats import E2M1_MAGNITUDES, e2m1_decode, e8m0_decode
 
 BLOCK = 32
+UOS_QMAX = 7.25
 
 
 def _floor_log2(a: np.ndarray) -> np.ndarray:
@@ -37,16 +45,29 @@ def _floor_log2(a: np.ndarray) -> np.ndarray:
     return e.astype(np.int64) - 1
 
 
-def block_scale_byte(amax) -> np.ndarray:
+def block_scale_byte(amax, rule: str = "ocp") -> np.ndarray:
     """E8M0 byte of the MX scale for block maxima ``amax`` (float64 >= 0, finite).
 
-    k = clamp(floor(log2 amax) - 2, -127, 127); byte = k + 127.  amax == 0 -> byte 0.
+    rule "ocp": k = floor(log2 amax) - 2.
+    rule "uos": k = the smallest integer with amax <= 7.25 * 2^k.  With e = floor(log2
+    amax) the candidates are e-3 .. e-1 (7.25 * 2^(e-3) < 2^e <= amax < 2^(e+1) <
+    7.25 * 2^(e-1)); each comparison is exact in float64 (7.25 * 2^k is a dyadic rational).
+    Both: k clamped to [-127, 127]; byte = k + 127; amax == 0 -> byte 0.
     """
     a = np.asarray(amax, dtype=np.float64)
     if not np.all(np.isfinite(a)) or np.any(a < 0):
         raise ValueError("block_scale_byte: amax must be finite and non-negative")
     safe = np.where(a > 0, a, 1.0)
-    k = np.where(a > 0, _floor_log2(safe) - 2, -127)
+    e = _floor_log2(safe)
+    if rule == "ocp":
+        k = e - 2
+    elif rule == "uos":
+        k = e - 1                                   # always satisfies the bound
+        for cand in (e - 2, e - 3):                 # the smallest candidate that still does
+            k = np.where(safe <= np.ldexp(UOS_QMAX, cand), cand, k)
+    else:
+        raise ValueError("block_scale_byte: rule must be 'ocp' or 'uos'")
+    k = np.where(a > 0, k, -127)
     k = np.clip(k, -127, 127)
     return (k + 127).astype(np.uint8)
 
@@ -75,11 +96,12 @@ def e2m1_encode(v) -> np.ndarray:
     return pick.astype(np.uint8) | sign
 
 
-def quantize_mxfp4(x):
+def quantize_mxfp4(x, rule: str = "ocp"):
     """MXFP4-quantize a 2-D array along its last axis (K).
 
     ``x``: float32 or float64 array [R, K] whose values are binary32-representable
-    (bf16 inputs are passed widened).  K must be a multiple of 32.
+    (bf16 inputs are passed widened).  K must be a multiple of 32.  ``rule``: block scale
+    rule, "ocp" or "uos" (see block_scale_byte).
     Returns (codes uint8 [R, K/2], scales uint8 [R, K/32]).
     """
     x = np.asarray(x)
@@ -93,7 +115,7 @@ def quantize_mxfp4(x):
         raise ValueError("quantize_mxfp4: non-finite input is outside the contract")
     blocks = x64.reshape(R, K // BLOCK, BLOCK)
     amax = np.max(np.abs(blocks), axis=2)
-    scales = block_scale_byte(amax)
+    scales = block_scale_byte(amax, rule)
     k = scales.astype(np.int64) - 127
     v = np.ldexp(blocks, -k[:, :, None])         # exact division by the power of two
     codes = e2m1_encode(v).reshape(R, K)
