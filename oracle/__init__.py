@@ -18,6 +18,7 @@ exact integer / rational arithmetic) unless the method fixes a precision:
 * ``gemm``     -- W4A4, W4A8 and bf16 reference GEMMs accumulated in float64, with the
   per-element error budget |gpu - oracle| <= 1e-5 * sum|a*b| + 1 bf16 ulp.
 * ``sqnr``     -- whole-output signal-to-quantization-noise ratio in dB.
+* ``hadamard`` -- the fixed block-Hadamard rotation ahead of MXFP4, in binary32.
 
 Sources (web pages, cited by title and section):
 * "AMD Quark adds native W4A8 mixed-precision for Wan2.2 video generation on MI350",
@@ -41,7 +42,7 @@ Parity status: every public function is pinned by the ``-m "not gpu"`` tests aga
 closed forms, library routines, exact rational brute force or invariants.
 """
 
-from . import formats, mxfp4, fp8, gemm, sqnr  # noqa: F401
+from . import formats, mxfp4, fp8, gemm, sqnr, hadamard  # noqa: F401
 from .formats import (  # noqa: F401
     E2M1_MAGNITUDES, e2m1_decode, e8m0_decode, e4m3_decode, E4M3_MAX,
     bf16_bits_to_f64, f64_to_bf16_bits, bf16_ulp,
@@ -52,3 +53,4 @@ from .gemm import (  # noqa: F401
     gemm_w4a4, gemm_w4a8, gemm_bf16, within_tolerance, tolerance_bound,
 )
 from .sqnr import sqnr_db  # noqa: F401
+from .hadamard import hadamard_matrix, rotate_f32, quantize_mxfp4_rotated  # noqa: F401
