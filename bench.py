@@ -244,7 +244,21 @@ def main():
     mxq.gemm_w4a4(ac, asc, wc_u, wsc_u, out=o44)
     r_u = mxq.sqnr(ref, o44, workspace=ws1)
     q_amount = work["mxq_quantize"][0]
+    # block-Hadamard rotation + MXFP4 of both operands (weights offline), n = 64 and 256
+    hada = {}
+    for n in (64, 256):
+        ms_h = time_fn(lambda: mxq.quantize_hadamard(a, n))
+        rwc, rwsc = mxq.quantize_hadamard(w, n)
+        rac, rasc = mxq.quantize_hadamard(a, n)
+        mxq.gemm_w4a4(rac, rasc, rwc, rwsc, out=o44)
+        r_h = mxq.sqnr(ref, o44, workspace=ws1)
+        rate = q_amount / (ms_h * 1e-3) / 1e9
+        hada[f"n{n}"] = {"mxq_quantize_hadamard": {"ms": round(ms_h, 4), "achieved": round(rate, 2), "unit": "GB/s",
+                                                   "peak": PEAK["hbm_GBps"], "frac": round(rate / PEAK["hbm_GBps"], 4)},
+                         "sqnr_db_w4a4": round(float(r_h[2].item()), 4)}
+        del rwc, rwsc, rac, rasc
     res["next"] = {
+        "hadamard_rotation": hada,
         "uos_scale_rule": {
             "mxq_quantize_uos": {"ms": round(ms_uos, 4), "achieved": round(q_amount / (ms_uos * 1e-3) / 1e9, 2),
                                  "unit": "GB/s", "peak": PEAK["hbm_GBps"],

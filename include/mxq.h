@@ -105,6 +105,23 @@ mxq_status mxq_quantize_rule(const void* x, mxq_dtype dt, int64_t rows, int64_t 
                              mxq_scale_rule rule, void* stream);
 
 /*
+ * mxq_quantize_hadamard -- fixed block-Hadamard rotation, then MXFP4 ([Q13] the data-free
+ * Hadamard transform of the block selector; [ORK] "Status": block-Hadamard with
+ * per-group scales).  Every run of block_n consecutive elements along a row becomes
+ * x H / sqrt(block_n) (H the Sylvester Hadamard matrix; block_n = 16, 64 or 256 so the
+ * normalisation is a power of two), formed in binary32 by the radix-2 butterfly in stage
+ * order h = 1, 2, 4, ... ((x_i, x_{i+h}) -> (x_i + x_{i+h}, x_i - x_{i+h}), each rounded),
+ * then quantized like binary32 input of mxq_quantize_rule.  Rotating activations here
+ * and weights with the same call leaves A W^T unchanged up to that rounding.
+ * Arguments, layout and errors as mxq_quantize_rule; cols must be a multiple of block_n
+ * (MXQ_ERR_INVALID_ARG); another block_n -> MXQ_ERR_UNSUPPORTED.
+ */
+mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
+                                 int block_n, mxq_scale_rule rule, uint8_t* codes, int64_t ld_codes,
+                                 uint8_t* scales, int64_t ld_scales, void* stream);
+
+/*
+ * mxq_quantize_fp8 --/*
  * mxq_quantize_fp8 -- static FP8 E4M3 activation quantization for W4A8 ([Q13]).
  *   q = E4M3(fl32(x * inv_scale)): one binary32 multiply (round to nearest even), then
  *   E4M3 round-to-nearest-even saturating at +-448 (never NaN); sign bit from the product.

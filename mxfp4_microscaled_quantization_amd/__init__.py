@@ -18,7 +18,7 @@ import numpy as np
 import torch
 
 __all__ = [
-    "lib", "MxqError", "quantize", "quantize_into", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
+    "lib", "MxqError", "quantize", "quantize_into", "quantize_hadamard", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
     "gemm_w4a4", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_workspace_bytes", "dequantize",
     "LIB_PATH", "ABI_SYMBOLS",
 ]
@@ -35,6 +35,8 @@ ABI_SYMBOLS = {
     "mxq_quantize": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, _ptr]),
     "mxq_quantize_rule": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _i64, _ptr, _i64, ctypes.c_int,
                                          _ptr]),
+    "mxq_quantize_hadamard": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, ctypes.c_int, ctypes.c_int, _ptr,
+                                             _i64, _ptr, _i64, _ptr]),
     "mxq_quantize_fp8": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _f32, _ptr, _i64, _ptr]),
     "mxq_absmax": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _ptr]),
     "mxq_gemm_w4a4": (ctypes.c_int, [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
@@ -138,6 +140,19 @@ def quantize_into(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, ru
     R, K = x.shape
     _check(lib.mxq_quantize_rule(_p(x), _dtype_code(x), R, K, ld, _p(codes), _rowmajor(codes, "codes"),
                                  _p(scales), _rowmajor(scales, "scales"), _rule_code(rule), _stream()))
+
+
+def quantize_hadamard(x: torch.Tensor, block_n: int = 64, rule: str = "ocp"):
+    """Rotate runs of ``block_n`` (16, 64, 256) elements of each row by H / sqrt(block_n)
+    (Sylvester Hadamard, binary32 butterfly), then MXFP4-quantize.  Returns (codes, scales)."""
+    _dev(x, "x")
+    ld = _rowmajor(x, "x")
+    R, K = x.shape
+    codes = torch.empty((R, K // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((R, K // 32), dtype=torch.uint8, device=x.device)
+    _check(lib.mxq_quantize_hadamard(_p(x), _dtype_code(x), R, K, ld, int(block_n), _rule_code(rule), _p(codes), K // 2,
+                                     _p(scales), K // 32, _stream()))
+    return codes, scales
 
 
 def fp8_static_scales(amax: float):

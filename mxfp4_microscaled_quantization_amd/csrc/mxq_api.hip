@@ -123,6 +123,29 @@ mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
   return mxq_quantize_rule(x, dt, rows, cols, ld_x, codes, ld_codes, scales, ld_scales, MXQ_SCALE_OCP, stream);
 }
 
+mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, int block_n,
+                                 mxq_scale_rule rule, uint8_t* codes, int64_t ld_codes, uint8_t* scales,
+                                 int64_t ld_scales, void* stream) {
+  const char* fn = "mxq_quantize_hadamard";
+  if (block_n != 16 && block_n != 64 && block_n != 256)
+    return fail(MXQ_ERR_UNSUPPORTED, "%s: block_n must be 16, 64 or 256 (got %d)", fn, block_n);
+  if (rule != MXQ_SCALE_OCP && rule != MXQ_SCALE_UOS)
+    return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown scale rule %d", fn, (int)rule);
+  mxq_status st = check_input(fn, x, dt, rows, cols, ld_x, 32);
+  if (st != MXQ_OK) return st;
+  if (cols % block_n != 0)
+    return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of block_n (%d)", fn, (long long)cols, block_n);
+  if (ld_codes < cols / 2) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_codes (%lld) < cols/2", fn, (long long)ld_codes);
+  if (ld_scales < cols / 32) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_scales (%lld) < cols/32", fn, (long long)ld_scales);
+  if (rows > 0 && cols > 0) {
+    if (!codes || !scales) return fail(MXQ_ERR_INVALID_ARG, "%s: codes/scales is NULL", fn);
+    if (!aligned(codes, 16) || ld_codes % 16 != 0)
+      return fail(MXQ_ERR_INVALID_ARG, "%s: codes base and ld_codes must be multiples of 16 bytes", fn);
+  }
+  return hip_status(fn, mxq::launch_quantize_mxfp4_rotated(x, dt == MXQ_F32, rows, cols, ld_x, block_n, codes, ld_codes,
+                                                           scales, ld_scales, rule == MXQ_SCALE_UOS, as_stream(stream)));
+}
+
 mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, float inv_scale,
                             uint8_t* q, int64_t ld_q, void* stream) {
   const char* fn = "mxq_quantize_fp8";

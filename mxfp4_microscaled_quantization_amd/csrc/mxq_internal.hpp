@@ -11,6 +11,9 @@ namespace mxq {
 hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
                                  uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
                                  bool uos, hipStream_t stream);
+hipError_t launch_quantize_mxfp4_rotated(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x, int n,
+                                         uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                                         bool uos, hipStream_t stream);
 hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
                                float inv_scale, uint8_t* q, int64_t ld_q, hipStream_t stream);
 hipError_t launch_absmax(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x, float* out,

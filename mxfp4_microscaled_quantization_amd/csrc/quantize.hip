@@ -20,6 +20,8 @@
 // gfx950 conversion v_cvt_scalef32_pk_fp4_f32, which computes round-to-nearest-even of
 // x / scale with saturation for power-of-two scales (including the subnormal 2^-127), two
 // elements per instruction (bf16 inputs are widened exactly first).
+#include <type_traits>
+
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -128,6 +130,140 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_kernel(
       if (ok[u]) {
         *reinterpret_cast<unsigned*>(codes + co[u]) = r;
         if (q == 0) scales[so[u]] = (uint8_t)s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Fixed block-Hadamard rotation, then MXFP4 ("AMD Quark adds native W4A8 mixed-precision
+// for Wan2.2 ...", section "Quark quantization pipeline and mixed-precision selection":
+// a fixed Hadamard rotation as the transform condition; "Exp 2026-08-22 W4A4 Reference
+// Model", section "Status": block-Hadamard with per-group scales).  Every run of N
+// consecutive elements along K becomes x H_N / sqrt(N) (Sylvester H_N, N = 16, 64, 256,
+// so 1/sqrt(N) is a power of two), formed in binary32 by the radix-2 butterfly in stage
+// order h = 1, 2, 4, ...: the pair (i, i + h) becomes (x_i + x_{i+h}, x_i - x_{i+h}).
+// The rotated values are then quantized as binary32 input.  Same lane mapping as
+// mx_quantize_kernel (4 lanes per 32-element block, 8 elements per lane): stages h < 8
+// stay in the lane, stages h >= 8 pair lane l with lane l ^ (h / 8).  A run never straddles
+// a row (K % N == 0) and starts at a multiple of N / 8 lanes.  Adds and the final scaling
+// are explicitly rounded (no contraction into fused operations).
+// value of lane l ^ D (D < 32): DPP inside a row of 16 lanes (quad permutes for 1 and 2,
+// row shifts for 4, a row rotation for 8), a permute through the LDS crossbar beyond
+template <int D>
+__device__ __forceinline__ float lane_xor(float v, int lane) {
+  const int b = __float_as_int(v);
+  if constexpr (D == 1) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
+  } else if constexpr (D == 2) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
+  } else if constexpr (D == 4) {
+    const int up = __builtin_amdgcn_mov_dpp(b, 0x104, 0xF, 0xF, true);          // row_shl:4 (lane + 4)
+    const int dn = __builtin_amdgcn_mov_dpp(b, 0x114, 0xF, 0xF, true);          // row_shr:4 (lane - 4)
+    return __int_as_float((lane & 4) ? dn : up);
+  } else if constexpr (D == 8) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));   // row_ror:8
+  } else {
+    return __shfl_xor(v, D);
+  }
+}
+
+template <bool F32, int N, bool UOS>
+__global__ __launch_bounds__(kThreads) void mx_quantize_rot_kernel(
+    const void* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ codes, int64_t ld_codes,
+    uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks,
+    int contiguous) {
+  static_assert(N == 16 || N == 64 || N == 256, "rotation runs of 16, 64 or 256");
+  constexpr float kNorm = N == 16 ? 0.25f : (N == 64 ? 0.125f : 0.0625f);   // 1 / sqrt(N)
+  const int tid = threadIdx.x;
+  const int q = tid & 3;
+  const int lane = tid & 63;
+  const int64_t stride = (int64_t)gridDim.x * kBlocksPerIter;
+  for (int64_t base = (int64_t)blockIdx.x * kBlocksPerIter; base < total_blocks; base += stride) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int64_t b = base + u * (kThreads / 4) + (tid >> 2);
+      const bool ok = b < total_blocks;
+      int64_t xo, co, so;
+      if (contiguous) {
+        xo = b * 32 + q * 8;
+        co = b * 16 + q * 4;
+        so = b;
+      } else {
+        const uint32_t bb = (uint32_t)b;
+        const uint32_t row = bb / blocks_per_row;
+        const uint32_t blk = bb - row * blocks_per_row;
+        xo = (int64_t)row * ld_x + blk * 32 + q * 8;
+        co = (int64_t)row * ld_codes + blk * 16 + q * 4;
+        so = (int64_t)row * ld_scales + blk;
+      }
+      float v[8];
+      if (F32) {
+        v4i d0 = v4i{0, 0, 0, 0}, d1 = v4i{0, 0, 0, 0};
+        if (ok) {
+          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
+          d0 = __builtin_nontemporal_load(p);
+          d1 = __builtin_nontemporal_load(p + 1);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[i] = __int_as_float(d0[i]);
+          v[4 + i] = __int_as_float(d1[i]);
+        }
+      } else {
+        v4i d0 = v4i{0, 0, 0, 0};
+        if (ok) d0 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = lo_f32(d0[i]);
+          v[2 * i + 1] = hi_f32(d0[i]);
+        }
+      }
+      // stages h = 1, 2, 4 inside the lane
+#pragma unroll
+      for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          if ((i & h) == 0) {
+            const float a = v[i], c = v[i + h];
+            v[i] = __fadd_rn(a, c);
+            v[i + h] = __fsub_rn(a, c);
+          }
+      // stages h = 8, 16, ... across lanes l and l ^ (h / 8); the lower index keeps the sum
+      auto cross = [&](auto d_tag) {
+        constexpr int D = decltype(d_tag)::value;
+        if constexpr (D < N / 8) {
+          const bool upper = (lane & D) != 0;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const float other = lane_xor<D>(v[i], lane);
+            v[i] = upper ? __fsub_rn(other, v[i]) : __fadd_rn(v[i], other);
+          }
+        }
+      };
+      cross(std::integral_constant<int, 1>{});
+      cross(std::integral_constant<int, 2>{});
+      cross(std::integral_constant<int, 4>{});
+      cross(std::integral_constant<int, 8>{});
+      cross(std::integral_constant<int, 16>{});
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = __fmul_rn(v[i], kNorm);
+      // MXFP4 of the rotated binary32 values (as mx_quantize_kernel)
+      unsigned m = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      const unsigned amax = quad_max_u32(m);
+      const unsigned e = amax >> 23;
+      const unsigned s = UOS ? scale_byte_uos(e, (amax & 0x7FFFFFu) > 0x680000u ? 1u : 0u) : scale_byte_from_exp(e);
+      const float scale = e8m0_to_f32(s);
+      unsigned r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], scale, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
+      if (ok) {
+        *reinterpret_cast<unsigned*>(codes + co) = r;
+        if (q == 0) scales[so] = (uint8_t)s;
       }
     }
   }
@@ -294,6 +430,38 @@ hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t 
     uos ? go(mx_quantize_kernel<true, true>) : go(mx_quantize_kernel<true, false>);
   else
     uos ? go(mx_quantize_kernel<false, true>) : go(mx_quantize_kernel<false, false>);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_mxfp4_rotated(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x, int n,
+                                         uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
+                                         bool uos, hipStream_t stream) {
+  const int64_t bpr = cols / 32;
+  const int64_t total = rows * bpr;
+  if (total == 0) return hipSuccess;
+  const int contiguous = (ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr) ? 1 : 0;
+  const int grid = grid_for(total, kBlocksPerIter);
+  auto go = [&](auto kernel) {
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes, ld_codes, scales, ld_scales,
+                       (uint32_t)bpr, total, contiguous);
+  };
+  auto pick_rule = [&](auto f32_tag, auto n_tag) {
+    constexpr bool F = decltype(f32_tag)::value;
+    constexpr int NN = decltype(n_tag)::value;
+    uos ? go(mx_quantize_rot_kernel<F, NN, true>) : go(mx_quantize_rot_kernel<F, NN, false>);
+  };
+  auto pick_n = [&](auto f32_tag) {
+    if (n == 16)
+      pick_rule(f32_tag, std::integral_constant<int, 16>{});
+    else if (n == 64)
+      pick_rule(f32_tag, std::integral_constant<int, 64>{});
+    else
+      pick_rule(f32_tag, std::integral_constant<int, 256>{});
+  };
+  if (f32)
+    pick_n(std::true_type{});
+  else
+    pick_n(std::false_type{});
   return hipGetLastError();
 }
 

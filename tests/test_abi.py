@@ -72,6 +72,9 @@ def _err():
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 16, 16, 16, FAKE, 8, FAKE, None), "workspace"),
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 16, 16, 16, FAKE, 1 << 20, None, None), "out3"),
     (lambda L: L.mxq_dequantize(FAKE, 16, FAKE, 1, 4, 48, FAKE, 48, None), "multiple of 32"),
+    (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 48, 48, FAKE, 32, FAKE, 2, 1, None), "multiple of 32"),
+    (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 96, 96, 64, 0, FAKE, 48, FAKE, 3, None), "multiple of block_n"),
+    (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 0, FAKE, 16, FAKE, 2, None), "ld_codes"),
 ])
 def test_invalid_arguments_are_rejected_before_launch(call, needle):
     st = call(mxq.lib)
@@ -82,6 +85,16 @@ def test_invalid_arguments_are_rejected_before_launch(call, needle):
 def test_unknown_dtype_is_unsupported():
     st = mxq.lib.mxq_quantize(FAKE, 7, 4, 64, 64, FAKE, 32, FAKE, 2, None)
     assert st == mxq.MXQ_ERR_UNSUPPORTED and "dtype" in _err()
+
+
+@pytest.mark.parametrize("call,needle", [
+    (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 64, 64, FAKE, 32, FAKE, 2, 5, None), "scale rule"),
+    (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 32, 0, FAKE, 32, FAKE, 2, None), "block_n"),
+    (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 3, FAKE, 32, FAKE, 2, None), "scale rule"),
+])
+def test_unknown_rule_or_block_is_unsupported(call, needle):
+    st = call(mxq.lib)
+    assert st == mxq.MXQ_ERR_UNSUPPORTED and needle in _err(), (st, _err())
 
 
 def test_empty_problems_are_noops():
