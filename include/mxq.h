@@ -158,6 +158,24 @@ mxq_status mxq_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
                          void* stream);
 
 /*
+ * mxq_gemm_w4a4_fused -- W4A4 with the dynamic activation quantization fused into the GEMM
+ * ([Q13] dynamic MXFP4 activations; [FLX] "MXFP4 quantization for diffusion models": the
+ * GEMM consumes MXFP4 with no separate conversion phase).  Equal, bit for bit, to
+ * mxq_quantize_rule(a, rule) followed by mxq_gemm_w4a4 on the result, without the
+ * quantized activations ever leaving the GPU's on-chip memory.
+ * a        : M x K activations of type `dt` (bf16 or binary32), row pitch ld_a elements;
+ *            base and row pitch (bytes) multiples of 16; finite values; 256 * ld_a * size
+ *            below 2^31 bytes.
+ * w_codes, w_scales, out_bf16, ld_out, K : as for mxq_gemm_w4a4.
+ * rule     : MXQ_SCALE_OCP or MXQ_SCALE_UOS (as mxq_quantize_rule).
+ * Errors as for mxq_quantize_rule and mxq_gemm_w4a4.
+ */
+mxq_status mxq_gemm_w4a4_fused(const void* a, mxq_dtype dt, int64_t ld_a,
+                               const uint8_t* w_codes, const uint8_t* w_scales,
+                               int64_t M, int64_t N, int64_t K, mxq_scale_rule rule,
+                               uint16_t* out_bf16, int64_t ld_out, void* stream);
+
+/*
  * mxq_gemm_w4a8 -- out = bf16_RNE( fl32( a_scale * sum_b 2^(SW[n,b] - 127) *
  *                  sum_{i<32} e4m3(QA8[m,32b+i]) * e2m1(QW[n,32b+i]) ) ) ([Q13] W4A8).
  * a_fp8   : M x K bytes (E4M3), contiguous rows, base 16-byte aligned.

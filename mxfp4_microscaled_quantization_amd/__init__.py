@@ -7,7 +7,7 @@ the library's gfx950 kernels.  Importing fails loudly if ``libmxq.so`` has not b
 built (``python mxfp4_microscaled_quantization_amd/build.py``); there is no fallback.
 
 Function names mirror the C entry points without the ``mxq_`` prefix:
-``quantize``, ``quantize_fp8``, ``absmax``, ``gemm_w4a4``, ``gemm_w4a8``, ``gemm_bf16``,
+``quantize``, ``quantize_fp8``, ``absmax``, ``gemm_w4a4``, ``gemm_w4a4_fused``, ``gemm_w4a8``, ``gemm_bf16``,
 ``sqnr``, ``dequantize``.  ``lib`` exposes the raw ctypes functions.
 """
 
@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "lib", "MxqError", "quantize", "quantize_into", "quantize_hadamard", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
-    "gemm_w4a4", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_workspace_bytes", "dequantize",
+    "gemm_w4a4", "gemm_w4a4_fused", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_workspace_bytes", "dequantize",
     "LIB_PATH", "ABI_SYMBOLS",
 ]
 
@@ -40,6 +40,8 @@ ABI_SYMBOLS = {
     "mxq_quantize_fp8": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _f32, _ptr, _i64, _ptr]),
     "mxq_absmax": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _ptr]),
     "mxq_gemm_w4a4": (ctypes.c_int, [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
+    "mxq_gemm_w4a4_fused": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _ptr, _ptr, _i64, _i64, _i64, ctypes.c_int, _ptr,
+                                           _i64, _ptr]),
     "mxq_gemm_w4a8": (ctypes.c_int, [_ptr, _f32, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_gemm_bf16": (ctypes.c_int, [_ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_sqnr_workspace_bytes": (_sz, [_i64]),
@@ -209,6 +211,23 @@ def gemm_w4a4(a_codes, a_scales, w_codes, w_scales, out=None):
         raise ValueError("inconsistent MXFP4 operand shapes")
     out, ld = _out(M, N, a_codes.device, out)
     _check(lib.mxq_gemm_w4a4(_p(a_codes), _p(a_scales), _p(w_codes), _p(w_scales), M, N, K, _p(out), ld, _stream()))
+    return out
+
+
+def gemm_w4a4_fused(a, w_codes, w_scales, rule: str = "ocp", out=None):
+    """W4A4 with the activation quantization fused in: bf16 or fp32 A [M, K] (rows may be
+    strided) x MXFP4 W [N, K]^T -> bf16 [M, N]; equal to gemm_w4a4(*quantize(a, rule), W)."""
+    _dev(a, "a")
+    ld = _rowmajor(a, "a")
+    for t, n in ((w_codes, "w_codes"), (w_scales, "w_scales")):
+        _contig(t, n, torch.uint8)
+    M, K = a.shape
+    N = w_codes.shape[0]
+    if w_codes.shape[1] * 2 != K or w_scales.shape != (N, K // 32):
+        raise ValueError("inconsistent operand shapes")
+    out, ldo = _out(M, N, a.device, out)
+    _check(lib.mxq_gemm_w4a4_fused(_p(a), _dtype_code(a), ld, _p(w_codes), _p(w_scales), M, N, K, _rule_code(rule),
+                                   _p(out), ldo, _stream()))
     return out
 
 

@@ -819,6 +819,482 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   }
 }
 
+// ---------------------------------------------------------------------------------
+// W4A4 with the dynamic activation quantization fused in ("AMD Quark adds native W4A8
+// mixed-precision for Wan2.2 ...", section "Quark quantization pipeline and mixed-precision
+// selection": activations are quantized to MXFP4 dynamically; "AMD Quark: 1.92x faster
+// FLUX.1-dev ...", section "MXFP4 quantization for diffusion models": the GEMM takes MXFP4
+// with no separate conversion phase).  Unquantized activations enter the GEMM; every
+// workgroup quantizes its own activation rows window by window into LDS -- codes in the
+// swizzled layout that the W4A4 kernels stage from HBM, scale bytes in a per-window
+// plane -- and runs the W4A4 MFMA steps on them in the same order, so each output is
+// bit-identical to mx_quantize_kernel followed by the W4A4 GEMM.
+//
+// The quantization is mx_quantize_kernel's: four lanes own a 32-element block (8 bf16 or
+// 4 binary32 ... per lane), the block maximum is an integer max over the sign-cleared
+// patterns reduced across the lanes of the block by DPP, the scale byte comes from its
+// exponent field, and the codes from the gfx950 scaled FP4 conversion of the exact
+// values (the bf16 form converts the same binary32 number the widened f32 form does).
+
+// One lane's 8 bf16 of a 32-element block held by 4 consecutive lanes -> 4 code bytes
+// (element 2j in the low nibble of byte j); s = the block's scale byte (equal across the
+// quad).  The quad maximum uses DPP operands of v_max_u32 directly; the scale is formed
+// as max(s << 23, 2^-127's pattern), the binary32 2^(s-127) for every s including 0.
+template <bool UOS>
+__device__ __forceinline__ unsigned mx_quant8_bf16(v4i d, unsigned& s) {
+  const unsigned d0 = (unsigned)d[0], d1 = (unsigned)d[1], d2 = (unsigned)d[2], d3 = (unsigned)d[3];
+  v2h m = __builtin_elementwise_max(__builtin_bit_cast(v2h, d0 & 0x7FFF7FFFu), __builtin_bit_cast(v2h, d1 & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(v2h, d2 & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(v2h, d3 & 0x7FFF7FFFu));
+  unsigned amax = max((unsigned)m[0], (unsigned)m[1]);
+  amax = max(amax, (unsigned)__builtin_amdgcn_mov_dpp((int)amax, 0xB1, 0xF, 0xF, true));   // lane ^ 1
+  amax = max(amax, (unsigned)__builtin_amdgcn_mov_dpp((int)amax, 0x4E, 0xF, 0xF, true));   // lane ^ 2
+  const unsigned e = amax >> 7;
+  if constexpr (UOS) {
+    s = scale_byte_uos(e, (amax & 0x7Fu) > 0x68u ? 1u : 0u);
+  } else {
+    const unsigned t = __builtin_elementwise_sub_sat(e, 2u);
+    s = e == 255u ? 255u : t;
+  }
+  const float scale = __uint_as_float(max(s << 23, 0x00400000u));
+  // byte 0 first; the other bytes of the first destination are overwritten after
+  unsigned r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(d0, __builtin_bit_cast(bf16x2, d0), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, d1), scale, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, d2), scale, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, d3), scale, 3);
+  return r;
+}
+
+// One lane's 4 binary32 of a 32-element block held by 8 consecutive lanes -> 2 code
+// bytes (low 16 bits); s = the block's scale byte.
+template <bool UOS>
+__device__ __forceinline__ unsigned mx_quant4_f32(v4i d, unsigned& s) {
+  unsigned m = max(max((unsigned)d[0] & 0x7FFFFFFFu, (unsigned)d[1] & 0x7FFFFFFFu),
+                   max((unsigned)d[2] & 0x7FFFFFFFu, (unsigned)d[3] & 0x7FFFFFFFu));
+  m = quad_max_u32(m);
+  const unsigned amax = max(m, (unsigned)__shfl_xor((int)m, 4));
+  const unsigned e = amax >> 23;
+  s = UOS ? scale_byte_uos(e, (amax & 0x7FFFFFu) > 0x680000u ? 1u : 0u) : scale_byte_from_exp(e);
+  const float scale = e8m0_to_f32(s);
+  unsigned r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d[0]), __int_as_float(d[1]), scale, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d[2]), __int_as_float(d[3]), scale, 1);
+  return r;
+}
+
+// Epilogue of the fused kernel (the fast kernels' epilogue): fp32 -> bf16 (RNE).  Runs
+// after the last hand-over barrier; the staged path reuses the first 128 KB of `lds`.
+__device__ __forceinline__ void store_tile_w4a4(const Params& p, v16f (&acc)[4][4], uint8_t* lds, uint32_t wave,
+                                                uint32_t lane, uint32_t wm, uint32_t wn, int m0, int n0) {
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+  if (p.vec16 && n0 + BN <= p.N) {
+    __syncthreads();
+    uint8_t* sub = lds + wave * (128u * 256u);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t row = 32 * j + r32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t chunk = 4 * i + pp;
+          *reinterpret_cast<v2u*>(sub + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * g) =
+              v2u{pack_bf16x2(acc[i][j][4 * pp + 0], acc[i][j][4 * pp + 1]),
+                  pack_bf16x2(acc[i][j][4 * pp + 2], acc[i][j][4 * pp + 3])};
+        }
+    }
+    const int mw = m0 + (int)wm * 128;
+    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+      const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
+      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
+      if (mw + (int)row < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)row * p.ld_out + c * 8) = v;
+    }
+    return;
+  }
+  const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + (int)(wm * 128 + 32 * j + r32);
+    uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
+        const unsigned lo = pack_bf16x2(acc[i][j][4 * pp + 0], acc[i][j][4 * pp + 1]);
+        const unsigned hi = pack_bf16x2(acc[i][j][4 * pp + 2], acc[i][j][4 * pp + 3]);
+        if (full) {
+          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+        } else if (m < p.M) {
+          if (p.vec_store && n + 4 <= p.N) {
+            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+          } else {
+            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
+            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
+            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
+            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Tile order shared by the fused kernels (the fast kernels' XCD-aware raster).
+__device__ __forceinline__ void tile_origin(const Params& p, int& m0, int& n0) {
+  const int nt = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int q8 = nt >> 3, r8 = nt & 7;
+  const int seq = xcd * q8 + min(xcd, r8) + local;
+  const int group = seq / (GROUP_M * p.tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(GROUP_M, p.tiles_m - first_m);
+  const int in_group = seq - group * GROUP_M * p.tiles_n;
+  m0 = (first_m + in_group % gm) * BM;
+  n0 = (in_group / gm) * BN;
+}
+
+// Generic fused kernel: any K (a multiple of 32), bf16 or binary32 activations, scale
+// planes of any alignment.  One LDS stage, register-staged weights; each window is
+// quantized in four passes, then its four MFMA steps run (no overlap).
+template <bool F32, bool UOS>
+__global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_generic_kernel(Params p) {
+  constexpr uint32_t A_TILE = BM * 128, W_TILE = BN * 128;
+  constexpr uint32_t AS_OFF = A_TILE + W_TILE;               // activation scale plane: [256 rows][8]
+  constexpr uint32_t STAGE = 4 * 128 * 256;                  // the epilogue's staging: 4 waves x 128 rows x 256 bytes
+  __shared__ __attribute__((aligned(16))) uint8_t lds[AS_OFF + BM * 8 > STAGE ? AS_OFF + BM * 8 : STAGE];
+  constexpr int W_CH = W_TILE / 16 / NT;                     // 8 chunks of 16 bytes per thread
+  constexpr int E = F32 ? 4 : 2;                             // bytes per activation element
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t wm = wave & 1, wn = wave >> 1;
+  int m0, n0;
+  tile_origin(p, m0, n0);
+  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w_scales + (int64_t)n0 * p.scale_row_bytes, rows_w * p.scale_row_bytes);
+  const uint32_t k_bytes = (uint32_t)p.scale_row_bytes * 32u * E;   // K elements in bytes
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const uint32_t w_c = tid % 8, w_r = tid / 8;
+  uint32_t sw_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) sw_off[i] = (wn * 128 + 32 * i + (lane & 31)) * p.scale_row_bytes;
+
+  for (int w = 0; w < p.nwin; ++w) {
+    // weights and their scales into registers
+    v4i stw[W_CH];
+    const uint32_t wbase = (uint32_t)w * 128 + w_c * 16;
+    const bool w_in = wbase + 16 <= p.w_row_bytes;
+#pragma unroll
+    for (int i = 0; i < W_CH; ++i)
+      stw[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_in ? (w_r + i * 32) * p.w_row_bytes + wbase : 0x80000000u, 0, 0);
+    uint32_t scw[4], sca[4];
+    const uint32_t col = (uint32_t)w * 8 + 4 * (lane >> 5);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scw[i] = load_scale4(rsw, sw_off[i], col, p.scale_row_bytes, p.scale_dword_ok);
+    __syncthreads();                     // the previous window's MFMAs are done with LDS
+#pragma unroll
+    for (int i = 0; i < W_CH; ++i) *reinterpret_cast<v4i*>(lds + A_TILE + swz128(w_r + i * 32, w_c)) = stw[i];
+    // activations: wave v quantizes rows 64v .. 64v+63, 16 rows per pass
+#pragma unroll 1
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (!F32) {
+        // a load covers 2 rows x 256 elements; lane l: row +l/32, elements 8 (l%32) ..
+        const uint32_t h = lane >> 5, b = (lane & 31) >> 2, k = lane & 3;
+        const uint32_t ebyte = (uint32_t)w * 512 + 16 * (lane & 31);
+        const bool in = ebyte + 16 <= k_bytes;
+        v4i d[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t row = 64 * wave + 16 * q + 2 * i + h;
+          d[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, in ? row * p.a_row_bytes + ebyte : 0x80000000u, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t row = 64 * wave + 16 * q + 2 * i + h;
+          unsigned s;
+          const unsigned c = mx_quant8_bf16<UOS>(d[i], s);
+          *reinterpret_cast<unsigned*>(lds + swz128(row, b) + 4 * k) = c;
+          if (k == 0) lds[AS_OFF + row * 8 + b] = (uint8_t)s;
+        }
+      } else {
+        // a load covers 1 row x 256 elements; lane l: elements 4l .. 4l+3
+        const uint32_t b = lane >> 3, k = lane & 7;
+        const uint32_t ebyte = (uint32_t)w * 1024 + 16 * lane;
+        const bool in = ebyte + 16 <= k_bytes;
+        v4i d[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t row = 64 * wave + 16 * q + i;
+          d[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, in ? row * p.a_row_bytes + ebyte : 0x80000000u, 0, 0);
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t row = 64 * wave + 16 * q + i;
+          unsigned s;
+          const unsigned c = mx_quant4_f32<UOS>(d[i], s);
+          *reinterpret_cast<uint16_t*>(lds + swz128(row, b) + 2 * k) = (uint16_t)c;
+          if (k == 0) lds[AS_OFF + row * 8 + b] = (uint8_t)s;
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      sca[j] = *reinterpret_cast<const uint32_t*>(lds + AS_OFF + (wm * 128 + 32 * j + (lane & 31)) * 8 + 4 * (lane >> 5));
+    mfma_step<GEMM_W4A4, 0>(acc, lds, lds + A_TILE, wm, wn, lane, scw, sca);
+    mfma_step<GEMM_W4A4, 1>(acc, lds, lds + A_TILE, wm, wn, lane, scw, sca);
+    mfma_step<GEMM_W4A4, 2>(acc, lds, lds + A_TILE, wm, wn, lane, scw, sca);
+    mfma_step<GEMM_W4A4, 3>(acc, lds, lds + A_TILE, wm, wn, lane, scw, sca);
+  }
+  store_tile_w4a4(p, acc, lds, wave, lane, wm, wn, m0, n0);
+}
+
+// Fast fused kernel (bf16 activations; K a whole number of 256-element windows; weight
+// scale rows and planes on 16-byte boundaries).  Weights and their scale chunks stream as
+// in gemm_fast_kernel<GEMM_W4A4> (two-slot weight ring, 32-byte scale chunks).  The
+// activation window w+1 is quantized during window w, a quarter per MFMA step: wave v
+// quantizes rows 64v + 16q .. +15 of quarter q, loaded into registers D steps earlier
+// (1 KB = 2 rows x 256 elements per load instruction), and writes 4 code bytes per lane
+// into the two-slot code ring and the block scale into a two-slot scale plane (lanes
+// that do not own a block's scale write into a sink beside it, so no lane branches).
+// Quarter 0 of window w+1 is quantized after the hand-over barrier of window w-1, which
+// releases its slot; quarters 1-3 under steps 0-2 of window w.
+//
+// Each MFMA step is issued as four units in source order, fenced from each other: 4
+// MFMAs, 2 fragment reads for the next step, 2 blocks quantized and stored, 2 activation
+// loads (and under the last step 2 weight-tile lines and a scale read).  The matrix core
+// works through a unit's MFMAs while the wave issues the unit's vector work.
+template <bool UOS, int D>
+__global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
+  static_assert(D == 2 || D == 4, "load lead of 2 or 4 steps");
+  constexpr uint32_t A_TILE = BM * 128, W_TILE = BN * 128;   // code tiles, 32 KB each
+  constexpr int W_LINES = (int)(W_TILE / 1024 / 4);           // 1 KB weight lines per wave per window
+  static_assert(W_LINES == 8, "two weight lines per unit");
+  constexpr uint32_t W_BASE = 2 * A_TILE;
+  constexpr uint32_t SC_ROW = 32;                             // weight scale chunk: 32 bytes per row
+  constexpr int CW = 4;                                       // windows per chunk
+  constexpr uint32_t SLOT = BN * SC_ROW;
+  constexpr int SC_LINES = (int)(SLOT / 1024 / 4);
+  constexpr uint32_t SC_BASE = W_BASE + 2 * W_TILE;
+  constexpr uint32_t AS_BASE = SC_BASE + 2 * SLOT;
+  constexpr uint32_t AS_SLOT = 4096;                          // [256 rows][8] scale bytes + 2 KB sink
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[AS_BASE + 2 * AS_SLOT];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const uint32_t wm = wave & 1, wn = wave >> 1;
+  int m0, n0;
+  tile_origin(p, m0, n0);
+  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w_scales + (int64_t)n0 * p.scale_row_bytes, rows_w * p.scale_row_bytes);
+  const uint32_t pitch = p.a_row_bytes;
+
+  // weight tile lines: 128-byte rows, 8 per 1 KB line; lane i lands at slot i % 8 of row
+  // i / 8 and fetches the chunk the swizzle puts there (even / odd lines differ)
+  const uint32_t wr = lane >> 3, wsl = lane & 7;
+  const uint32_t w_voff0 = wr * p.w_row_bytes + ((wsl ^ ((wr >> 1) & 7u)) * 16);
+  const uint32_t w_voff1 = wr * p.w_row_bytes + ((wsl ^ (((8u + wr) >> 1) & 7u)) * 16);
+  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
+  // activation loads and code / scale writes: load i of a quarter covers rows 2i, 2i+1
+  // (lane / 32) of the wave's 16, elements 8 (lane % 32) ..; the code slot of row r,
+  // block b is b ^ ((r >> 1) & 7) = b ^ i
+  const uint32_t h = lane >> 5, b = (lane & 31) >> 2, k = lane & 3;
+  const uint32_t a_voff = h * pitch + 16 * (lane & 31);
+  const uint32_t cw0 = wave * 8192u + h * 128u + 4u * k + (b << 4);
+  const uint32_t sw0 = k == 0 ? wave * 512u + h * 8u + b : 2048u + lane;
+
+  auto issue_w_line = [&](int w, int par, int j) {
+    const uint32_t line = wave * W_LINES + j;
+    load_line_to_lds(rw, lds + W_BASE + (uint32_t)par * W_TILE + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+                     (uint32_t)w * 128 + line * 8 * p.w_row_bytes);
+  };
+  const int nwin = p.nwin;
+  const int nchunks = (nwin + CW - 1) / CW;
+  auto issue_chunk = [&](int c) {
+    uint8_t* slot = lds + SC_BASE + (uint32_t)(c & 1) * SLOT;
+#pragma unroll
+    for (int j = 0; j < SC_LINES; ++j) {
+      const uint32_t line = wave * SC_LINES + j;
+      load_line_to_lds(rsw, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + line * 32 * p.scale_row_bytes);
+    }
+  };
+  // chunk c+1 goes out at the start of window c*CW (c >= 1): every wave has passed its
+  // last read of chunk c-1, the slot's previous occupant
+  auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
+  auto read_w_scale = [&](int w, uint32_t ln, int i) {
+    const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
+    const uint32_t col = (uint32_t)(w % CW) * 8 + 4 * (ln >> 5);
+    return *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i + (ln & 31)) * SC_ROW + col);
+  };
+  auto read_a_scale = [&](int par, uint32_t ln, int j) {
+    return *reinterpret_cast<const uint32_t*>(lds + AS_BASE + (uint32_t)par * AS_SLOT +
+                                              (wm * 128 + 32 * j + (ln & 31)) * 8 + 4 * (ln >> 5));
+  };
+  // fragment kk (0-3: weight rows, 4-7: activation rows) of MFMA step t from slot `par`
+  auto read_frag = [&](int par, uint32_t ln, int t, int kk) {
+    const uint32_t chunk = (ln >> 5) * 4 + t;
+    const uint8_t* base = kk < 4 ? lds + W_BASE + (uint32_t)par * W_TILE : lds + (uint32_t)par * A_TILE;
+    const uint32_t row = (kk < 4 ? wn : wm) * 128 + 32 * (kk & 3) + (ln & 31);
+    return *reinterpret_cast<const v4i*>(base + swz128(row, chunk));
+  };
+  // load i of quarter q of activation window v
+  auto load_act = [&](int v, int q, int i) {
+    return __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, (uint32_t)(64 * wave + 16 * q + 2 * i) * pitch + (uint32_t)v * 512u,
+                                                 0);
+  };
+  // quantize load i of quarter q into code / scale slot `par`
+  auto quant_act = [&](int par, int q, int i, v4i d) {
+    unsigned s;
+    const unsigned c = mx_quant8_bf16<UOS>(d, s);
+    *reinterpret_cast<unsigned*>(lds + (uint32_t)par * A_TILE + q * 2048 + 256 * i + (cw0 ^ ((uint32_t)i << 4))) = c;
+    lds[AS_BASE + (uint32_t)par * AS_SLOT + q * 128 + 16 * i + sw0] = (uint8_t)s;
+  };
+
+  v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  // prologue: weight window 0 and chunk 0 in flight; activation window 0 and quarter 0 of
+  // window 1 quantized one quarter at a time; then chunk 1, the first D quarters of the
+  // steady-state lead and weight window 1 in flight, in the order the steady state keeps
+  // them (loads past the last window read zeros or unused bytes, and nothing reads what
+  // they deliver); step-0 fragments and scales read.
+#pragma unroll
+  for (int j = 0; j < W_LINES; ++j) issue_w_line(0, 0, j);
+  issue_chunk(0);
+#pragma unroll
+  for (int Q = 0; Q < 5; ++Q) {
+    v4i d[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) d[i] = load_act(Q / 4, Q % 4, i);
+    if (Q / 4 < nwin) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) quant_act((Q / 4) & 1, Q % 4, i, d[i]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  issue_chunk(1);
+  v4i stg[D][8];
+#pragma unroll
+  for (int Q = 5; Q < 5 + D; ++Q)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) stg[(Q % 4) % D][i] = load_act(Q / 4, Q % 4, i);
+#pragma unroll
+  for (int j = 0; j < W_LINES; ++j) issue_w_line(1, 1, j);
+  uint32_t scw[4], sca[4];
+  v4i f0[8], f1[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) f0[kk] = read_frag(0, lane, 0, kk);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    scw[i] = read_w_scale(0, lane, i);
+    sca[i] = read_a_scale(0, lane, i);
+  }
+
+  // One window w with slot parity PAR = w & 1 (a constant in the steady state).  Region r (the MFMAs of step r) quantizes
+  // global quarter 4w + r + 5 (window w+1 quarters 1..3, then window w+2 quarter 0) from
+  // the registers loaded D regions earlier and loads quarter 4w + r + 5 + D into them.
+  // TAIL windows check each against the window count and drain all loads at the hand-over.
+  auto window = [&](int w, int PAR, auto tail_tag) {
+    constexpr bool TAIL = decltype(tail_tag)::value;
+    uint32_t ln = lane;
+    asm volatile("" : "+v"(ln));
+    if (chunk_due(w)) issue_chunk(w / CW + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t scw_n[4], sca_n[4];
+    auto region = [&](auto r_tag, v4i (&fc)[8], v4i (&fn)[8]) {
+      constexpr int R = decltype(r_tag)::value;
+      constexpr int QC = (R + 1) & 3, VC = (R + 5) >> 2;           // quarter quantized: window w + VC
+      constexpr int QL = (R + 1 + D) & 3, VL = (R + 5 + D) >> 2;   // quarter loaded: window w + VL
+      constexpr int IX = QC % D;
+      static_assert(QL % D == IX, "ring slot");
+      const int PC = (PAR + VC) & 1;                               // code / scale slot quantized into
+      const bool q_ok = !TAIL || w + VC < nwin;
+      const bool l_ok = !TAIL || w + VL < nwin;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[u][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fc[u]), widen(fc[4 + j]), acc[u][j], 4, 4,
+                                                                      R, (int)scw[u], R, (int)sca[j]);
+        if constexpr (R < 3) {
+          fn[2 * u] = read_frag(PAR, ln, R + 1, 2 * u);
+          fn[2 * u + 1] = read_frag(PAR, ln, R + 1, 2 * u + 1);
+          if constexpr (R == 1) scw_n[u] = read_w_scale(w + 1, ln, u);
+        } else {
+          fn[2 * u] = read_frag(PAR ^ 1, ln, 0, 2 * u);
+          if (!TAIL || w + 2 < nwin) issue_w_line(w + 2, PAR, 2 * u);
+          fn[2 * u + 1] = read_frag(PAR ^ 1, ln, 0, 2 * u + 1);
+          if (!TAIL || w + 2 < nwin) issue_w_line(w + 2, PAR, 2 * u + 1);
+          sca_n[u] = read_a_scale(PAR ^ 1, ln, u);
+        }
+        if (q_ok) {
+          quant_act(PC, QC, 2 * u, stg[IX][2 * u]);
+          quant_act(PC, QC, 2 * u + 1, stg[IX][2 * u + 1]);
+        }
+        if (l_ok) {
+          stg[IX][2 * u] = load_act(w + VL, QL, 2 * u);
+          stg[IX][2 * u + 1] = load_act(w + VL, QL, 2 * u + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    region(std::integral_constant<int, 0>{}, f0, f1);
+    region(std::integral_constant<int, 1>{}, f1, f0);
+    region(std::integral_constant<int, 2>{}, f0, f1);
+    // hand-over: weight window w+1 landed (at least 16 activation loads went out after
+    // it), this wave's code and scale writes for window w+1 done; then every wave is past
+    // its reads of window w's slots
+    if constexpr (TAIL)
+      __builtin_amdgcn_s_waitcnt(0);
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    region(std::integral_constant<int, 3>{}, f1, f0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      scw[i] = scw_n[i];
+      sca[i] = sca_n[i];
+    }
+  };
+  constexpr int TAIL_WINDOWS = D == 2 ? 2 : 3;
+  const int steady = nwin - TAIL_WINDOWS;
+  int w = 0;
+  for (; w + 1 < steady; w += 2) {
+    window(w, 0, std::false_type{});
+    window(w + 1, 1, std::false_type{});
+  }
+  if (w < steady) {
+    window(w, 0, std::false_type{});
+    ++w;
+  }
+  for (; w < nwin; ++w) window(w, w & 1, std::true_type{});
+
+  store_tile_w4a4(p, acc, lds, wave, lane, wm, wn, m0, n0);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,
@@ -868,6 +1344,55 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
     case GEMM_BF16:
       launch(std::integral_constant<int, GEMM_BF16>{}, (uint32_t)(K * 2), (uint32_t)(K * 2), false);
       break;
+  }
+  return hipGetLastError();
+}
+
+
+hipError_t launch_gemm_w4a4_fused(const void* a, bool f32, int64_t ld_a, const uint8_t* w, const uint8_t* w_scales,
+                                  int64_t M, int64_t N, int64_t K, bool uos, uint16_t* out, int64_t ld_out,
+                                  hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  Params p;
+  p.a = static_cast<const uint8_t*>(a);
+  p.a_scales = nullptr;
+  p.w = w;
+  p.w_scales = w_scales;
+  p.out = out;
+  p.ld_out = ld_out;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.a_row_bytes = (uint32_t)(ld_a * (f32 ? 4 : 2));
+  p.w_row_bytes = (uint32_t)(K / 2);
+  p.scale_row_bytes = (uint32_t)(K / 32);
+  auto aligned_to = [](const void* q, uintptr_t al) { return (reinterpret_cast<uintptr_t>(q) % al) == 0; };
+  p.scale_dword_ok = ((K / 32) % 4 == 0 && aligned_to(w_scales, 4)) ? 1 : 0;
+  p.a_scale = 1.0f;
+  p.vec_store = (ld_out % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 7) == 0) ? 1 : 0;
+  p.vec16 = (ld_out % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) ? 1 : 0;
+  p.tiles_m = (int)((M + BM - 1) / BM);
+  p.tiles_n = (int)((N + BN - 1) / BN);
+  const dim3 grid((unsigned)(p.tiles_m * p.tiles_n)), block(NT);
+  const bool fast = !f32 && K > 0 && K % 256 == 0 && (K / 32) % 16 == 0 && aligned_to(w_scales, 16);
+  if (fast) {
+    p.nwin = (int)(K / 256);
+    if (uos)
+      hipLaunchKernelGGL((gemm_w4a4_fused_kernel<true, 2>), grid, block, 0, stream, p);
+    else
+      hipLaunchKernelGGL((gemm_w4a4_fused_kernel<false, 2>), grid, block, 0, stream, p);
+  } else {
+    p.nwin = (int)((K + 255) / 256);
+    if (f32) {
+      if (uos)
+        hipLaunchKernelGGL((gemm_w4a4_fused_generic_kernel<true, true>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_w4a4_fused_generic_kernel<true, false>), grid, block, 0, stream, p);
+    } else {
+      if (uos)
+        hipLaunchKernelGGL((gemm_w4a4_fused_generic_kernel<false, true>), grid, block, 0, stream, p);
+      else
+        hipLaunchKernelGGL((gemm_w4a4_fused_generic_kernel<false, false>), grid, block, 0, stream, p);
+    }
   }
   return hipGetLastError();
 }

@@ -188,6 +188,28 @@ mxq_status mxq_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const 
                                          out_bf16, ld_out, as_stream(stream)));
 }
 
+mxq_status mxq_gemm_w4a4_fused(const void* a, mxq_dtype dt, int64_t ld_a, const uint8_t* w_codes,
+                               const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, mxq_scale_rule rule,
+                               uint16_t* out_bf16, int64_t ld_out, void* stream) {
+  const char* fn = "mxq_gemm_w4a4_fused";
+  if (rule != MXQ_SCALE_OCP && rule != MXQ_SCALE_UOS)
+    return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown scale rule %d", fn, (int)rule);
+  if (dtype_bytes(dt) == 0) return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown dtype %d", fn, (int)dt);
+  mxq_status st = check_gemm(fn, M, N, K, out_bf16, ld_out);
+  if (st != MXQ_OK) return st;
+  if (M > 0 && N > 0) {
+    if ((st = check_input(fn, a, dt, M, K, ld_a, 32)) != MXQ_OK) return st;
+    if (ld_a * dtype_bytes(dt) * 256 >= ((int64_t)1 << 31))
+      return fail(MXQ_ERR_INVALID_ARG, "%s: row pitch too large (256 * ld_a * element size must be below 2^31 bytes)",
+                  fn);
+    if ((st = check_operand(fn, "w_codes", w_codes, N, K, 16)) != MXQ_OK) return st;
+    if ((st = check_operand(fn, "w_scales", w_scales, N, K, 1)) != MXQ_OK) return st;
+    if (K > 0 && !a) return fail(MXQ_ERR_INVALID_ARG, "%s: a is NULL", fn);
+  }
+  return hip_status(fn, mxq::launch_gemm_w4a4_fused(a, dt == MXQ_F32, ld_a, w_codes, w_scales, M, N, K,
+                                                    rule == MXQ_SCALE_UOS, out_bf16, ld_out, as_stream(stream)));
+}
+
 mxq_status mxq_gemm_w4a8(const uint8_t* a_fp8, float a_scale, const uint8_t* w_codes, const uint8_t* w_scales,
                          int64_t M, int64_t N, int64_t K, uint16_t* out_bf16, int64_t ld_out, void* stream) {
   const char* fn = "mxq_gemm_w4a8";

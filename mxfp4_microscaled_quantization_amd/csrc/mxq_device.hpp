@@ -44,4 +44,17 @@ __device__ __forceinline__ float e8m0_to_f32(unsigned s) {
   return __uint_as_float(s ? (s << 23) : 0x00400000u);
 }
 
+// MXFP4 scale byte from the biased exponent field e of the block maximum: the OCP rule
+// s = max(e - 2, 0); non-finite blocks (e == 255) get the E8M0 NaN.
+__device__ __forceinline__ unsigned scale_byte_from_exp(unsigned e) {
+  return e == 255u ? 255u : (e > 2u ? e - 2u : 0u);
+}
+
+// The UOS rule: one more when the significand of a normal maximum exceeds 1.8125
+// (bump = 1), floored at 0 like the OCP rule.
+__device__ __forceinline__ unsigned scale_byte_uos(unsigned e, unsigned bump) {
+  const unsigned t = e + (e != 0u ? bump : 0u);
+  return e == 255u ? 255u : (t > 2u ? t - 2u : 0u);
+}
+
 }  // namespace mxq

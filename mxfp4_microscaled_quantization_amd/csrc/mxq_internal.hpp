@@ -27,6 +27,12 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
                        const uint8_t* w_scales, float a_scale, int64_t M, int64_t N, int64_t K,
                        uint16_t* out, int64_t ld_out, hipStream_t stream);
 
+// W4A4 with the activation quantization fused in: `a` is rows x K of bf16 (or binary32),
+// pitch ld_a elements; uos selects the UOS scale rule.
+hipError_t launch_gemm_w4a4_fused(const void* a, bool f32, int64_t ld_a, const uint8_t* w, const uint8_t* w_scales,
+                                  int64_t M, int64_t N, int64_t K, bool uos, uint16_t* out, int64_t ld_out,
+                                  hipStream_t stream);
+
 size_t sqnr_workspace_bytes(int64_t n);
 hipError_t launch_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols,
                        int64_t ld_ref, int64_t ld_test, void* ws, double* out3, hipStream_t stream);

@@ -35,17 +35,6 @@ constexpr int kBlocksPerIter = kThreads / 4 * kUnroll;
 __device__ __forceinline__ float lo_f32(int pair) { return __uint_as_float((unsigned)pair << 16); }
 __device__ __forceinline__ float hi_f32(int pair) { return __uint_as_float((unsigned)pair & 0xFFFF0000u); }
 
-__device__ __forceinline__ unsigned scale_byte_from_exp(unsigned e) {
-  // e: biased exponent field of amax.  Non-finite blocks (e == 255) get the E8M0 NaN.
-  return e == 255u ? 255u : (e > 2u ? e - 2u : 0u);
-}
-
-// UOS: one more when the significand of a normal amax exceeds 1.8125 (bump = 1)
-__device__ __forceinline__ unsigned scale_byte_uos(unsigned e, unsigned bump) {
-  const unsigned t = e + (e != 0u ? bump : 0u);
-  return e == 255u ? 255u : (t > 2u ? t - 2u : 0u);
-}
-
 // ---------------------------------------------------------------------------------
 // MXFP4 quantization.  F32 selects binary32 input (else bf16); UOS the 7.25 boundary.
 template <bool F32, bool UOS>

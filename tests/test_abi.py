@@ -75,6 +75,14 @@ def _err():
     (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 48, 48, FAKE, 32, FAKE, 2, 1, None), "multiple of 32"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 96, 96, 64, 0, FAKE, 48, FAKE, 3, None), "multiple of block_n"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 0, FAKE, 16, FAKE, 2, None), "ld_codes"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 48, FAKE, FAKE, 8, 8, 48, 0, FAKE, 8, None), "multiple of 32"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 32, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "ld_x"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 68, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "aligned"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE_ODD, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "aligned"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 0, 1 << 21, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "row pitch"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, None, FAKE, 8, 8, 64, 0, FAKE, 8, None), "w_codes is NULL"),
+    (lambda L: L.mxq_gemm_w4a4_fused(None, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "NULL"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 4, None), "ld_out"),
 ])
 def test_invalid_arguments_are_rejected_before_launch(call, needle):
     st = call(mxq.lib)
@@ -91,6 +99,8 @@ def test_unknown_dtype_is_unsupported():
     (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 64, 64, FAKE, 32, FAKE, 2, 5, None), "scale rule"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 32, 0, FAKE, 32, FAKE, 2, None), "block_n"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 3, FAKE, 32, FAKE, 2, None), "scale rule"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 2, FAKE, 8, None), "scale rule"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 9, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "dtype"),
 ])
 def test_unknown_rule_or_block_is_unsupported(call, needle):
     st = call(mxq.lib)
@@ -101,6 +111,7 @@ def test_empty_problems_are_noops():
     assert mxq.lib.mxq_quantize(None, 1, 0, 64, 64, None, 32, None, 2, None) == mxq.MXQ_OK
     assert mxq.lib.mxq_gemm_w4a4(None, None, None, None, 0, 8, 64, None, 8, None) == mxq.MXQ_OK
     assert mxq.lib.mxq_gemm_w4a8(None, ctypes.c_float(1.0), None, None, 8, 0, 64, None, 0, None) == mxq.MXQ_OK
+    assert mxq.lib.mxq_gemm_w4a4_fused(None, 1, 64, None, None, 0, 8, 64, 0, None, 8, None) == mxq.MXQ_OK
     assert _err() == ""
 
 
