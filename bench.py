@@ -257,7 +257,22 @@ def main():
                                                    "peak": PEAK["hbm_GBps"], "frac": round(rate / PEAK["hbm_GBps"], 4)},
                          "sqnr_db_w4a4": round(float(r_h[2].item()), 4)}
         del rwc, rwsc, rac, rasc
+    # W4A4 with the activation quantization fused into the GEMM (bf16 activations in),
+    # against the separate quantize + W4A4 of the timed step, and checked bit for bit
+    o_f = torch.empty_like(o44)
+    ms_f = time_fn(lambda: mxq.gemm_w4a4_fused(a, wc, wsc, out=o_f))
+    mxq.quantize_into(a, ac, asc)
+    mxq.gemm_w4a4(ac, asc, wc, wsc, out=o44)
+    torch.cuda.synchronize()
+    fused_same = bool(torch.equal(o_f.view(torch.int16), o44.view(torch.int16)))
+    del o_f
+    rate_f = flop / (ms_f * 1e-3) / 1e12
+    fused = {"mxq_gemm_w4a4_fused": {"ms": round(ms_f, 4), "achieved": round(rate_f, 2), "unit": "TFLOP/s",
+                                     "peak": PEAK["fp4_TFLOPs"], "frac": round(rate_f / PEAK["fp4_TFLOPs"], 4)},
+             "quantize_plus_w4a4_ms": round(per_kernel_ms["mxq_quantize"] + per_kernel_ms["mxq_gemm_w4a4"], 4),
+             "bit_identical_to_quantize_then_w4a4": fused_same}
     res["next"] = {
+        "fused_activation_quant": fused,
         "hadamard_rotation": hada,
         "uos_scale_rule": {
             "mxq_quantize_uos": {"ms": round(ms_uos, 4), "achieved": round(q_amount / (ms_uos * 1e-3) / 1e9, 2),

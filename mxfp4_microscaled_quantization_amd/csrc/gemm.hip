@@ -28,10 +28,15 @@
 //  * Workgroups are renumbered so that each XCD (dispatched round-robin) walks a
 //    contiguous run of tiles, grouped 4 m-tiles wide, keeping panels shared in its L2.
 //  * Ragged M/N/K tails are zero-filled by buffer-load range checks and masked stores.
+//  * The bf16 reference runs an eight-wave variant (two waves per SIMD, 64 x 128 per
+//    wave), which issues its memory and LDS instructions alongside the other wave's MFMAs.
+//  * gemm_w4a4_fused8_kernel takes unquantized activations and quantizes each activation
+//    tile into LDS inside the GEMM, bit-identically to the separate quantizer.
 #include <type_traits>
 
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
+
 
 namespace mxq {
 namespace {
@@ -1062,40 +1067,459 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_generic_kernel(Params p
   store_tile_w4a4(p, acc, lds, wave, lane, wm, wn, m0, n0);
 }
 
+// ---------------------------------------------------------------------------------
+// Eight-wave fast path: the same pipeline as gemm_fast_kernel with two waves per SIMD.
+// A wave issues at most one instruction per few cycles whatever its type, and a second
+// wave on the SIMD issues in parallel, so the DMA, scale and LDS-read instructions of one
+// wave no longer hold back the matrix core while the other wave's MFMAs run.  Each wave
+// owns a 64 (m) x 128 (n) sub-tile: 4 weight fragments x 2 activation fragments, 8
+// accumulators (128 AGPRs), 8 MFMAs per step.  Every 32 x 32 output block still gets the
+// same MFMAs in the same order as in the four-wave kernel.
+constexpr int NT8 = 512;
+
+// Fragments of MFMA step t for the eight-wave layout: weight rows wn*128 + 32i (i < 4)
+// into f[0..3], activation rows wm*64 + 32j (j < 2) into f[4..5] (FP8: low halves
+// f[4..5], high halves f[6..7]).  `after(k)` runs after the k-th read.
+template <int MODE, class After>
+__device__ __forceinline__ void read_frags8(v4i (&f)[8], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
+                                            uint32_t lane, int t, After&& after) {
+  using F = Fast<MODE>;
+  const uint32_t g = lane >> 5, r32 = lane & 31;
+  const uint32_t chunk = g * F::STEPS + t;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    f[i] = *reinterpret_cast<const v4i*>(lw + swz<F::W_RB>(wn * 128 + 32 * i + r32, chunk));
+    after(i);
+  }
+  if constexpr (MODE == GEMM_W4A8) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = wm * 64 + 32 * j + r32;
+      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 2 * t + g));
+      after(4 + 2 * j);
+      f[6 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 4 + 2 * t + g));
+      after(5 + 2 * j);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz<F::A_RB>(wm * 64 + 32 * j + r32, chunk));
+      after(4 + j);
+    }
+  }
+}
+
+template <int MODE>
+__device__ __forceinline__ void read_frags8(v4i (&f)[8], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
+                                            uint32_t lane, int t) {
+  read_frags8<MODE>(f, la, lw, wm, wn, lane, t, [](int) {});
+}
+
+template <int MODE, int T>
+__device__ __forceinline__ void mfma8(v16f (&acc)[4][2], const v4i (&f)[8], const uint32_t (&scw)[4],
+                                      const uint32_t (&sca)[2]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if constexpr (MODE == GEMM_W4A4)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), widen(f[4 + j]), acc[i][j], 4, 4, T,
+                                                                    (int)scw[i], T, (int)sca[j]);
+      else if constexpr (MODE == GEMM_W4A8)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), cat(f[4 + j], f[6 + j]), acc[i][j],
+                                                                    4, 0, T, (int)scw[i], 0, 127);
+      else
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                            __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
+    }
+}
+
+// One scheduling region of the eight-wave kernel: `reads` LDS reads, `vm` DMA loads spread
+// over them (dma_after), 8 MFMAs.
+template <int READS, int VM>
+__device__ __forceinline__ void interleave8() {
+  constexpr int N = READS > 8 ? READS : 8;
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    if (r < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (r < READS && VM > 0 && dma_after(r, VM, READS) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    if (r < 8) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(NT8, 1) void gemm_fast8_kernel(Params p) {
+  using C = Fast<MODE>;
+  constexpr int WAVES = NT8 / 64;
+  constexpr uint32_t A_TILE = BM * C::A_RB;
+  constexpr uint32_t W_TILE = BN * C::W_RB;
+  constexpr int A_LINES = A_TILE / 1024 / WAVES;   // 1 KB LDS lines per wave per window
+  constexpr int W_LINES = W_TILE / 1024 / WAVES;
+  constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
+  constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
+  constexpr int NA = C::NA, NW = C::NW;
+  constexpr bool SPLIT = NA != NW;
+  static_assert(!SPLIT || (NA == 3 && NW == 2), "split rings: three activation, two weight slots");
+  constexpr int NS = NA;
+  constexpr uint32_t W_BASE = NA * A_TILE, SC_BASE = NA * A_TILE + NW * W_TILE;
+  constexpr uint32_t SC_WIN = C::SC_WIN;
+  constexpr bool HAS_SC = SC_WIN > 0;
+  constexpr uint32_t SC_ROW = 32;
+  constexpr int CW = HAS_SC ? (int)(SC_ROW / SC_WIN) : 1;
+  constexpr uint32_t SC_ROWS = HAS_SC ? BN + (MODE == GEMM_W4A4 ? BM : 0) : 0;
+  constexpr uint32_t SLOT = SC_ROWS * SC_ROW;
+  constexpr int SC_LINES = (int)(SLOT / 1024 / WAVES);
+  static_assert(!HAS_SC || SC_LINES >= 1, "a scale chunk line per wave");
+  constexpr uint32_t LDS_BYTES = SC_BASE + 2 * SLOT > 8u * 16384u ? SC_BASE + 2 * SLOT : 8u * 16384u;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+
+  const uint32_t tid = threadIdx.x, lane = tid & 63;
+  const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const uint32_t wm = wave & 3, wn = wave >> 2;
+
+  int m0, n0;
+  tile_origin(p, m0, n0);
+  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
+  const bool has_ws = MODE != GEMM_BF16, has_as = MODE == GEMM_W4A4;
+  const __amdgpu_buffer_rsrc_t rsw =
+      make_rsrc(has_ws ? p.w_scales + (int64_t)n0 * p.scale_row_bytes : p.w, has_ws ? rows_w * p.scale_row_bytes : 0);
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc(has_as ? p.a_scales + (int64_t)m0 * p.scale_row_bytes : p.a, has_as ? rows_a * p.scale_row_bytes : 0);
+
+  constexpr uint32_t A_CPR = C::A_RB / 16, W_CPR = C::W_RB / 16;
+  auto dma_voffs = [&](uint32_t cpr, uint32_t row_bytes, uint32_t& even, uint32_t& odd) {
+    const uint32_t row = lane / cpr, slot = lane % cpr;
+    if (cpr == 8) {
+      even = row * row_bytes + ((slot ^ ((row >> 1) & 7u)) * 16);
+      odd = row * row_bytes + ((slot ^ (((8u + row) >> 1) & 7u)) * 16);
+    } else {
+      even = odd = row * row_bytes + ((slot ^ ((row >> 2) & 3u)) * 16);
+    }
+  };
+  uint32_t a_voff0, a_voff1, w_voff0, w_voff1;
+  dma_voffs(A_CPR, p.a_row_bytes, a_voff0, a_voff1);
+  dma_voffs(W_CPR, p.w_row_bytes, w_voff0, w_voff1);
+  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
+
+  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NA) * A_TILE; };
+  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NW) * W_TILE; };
+  auto issue_line = [&](int w, auto part_tag, int j) {
+    constexpr int PART = decltype(part_tag)::value;
+    if constexpr (PART == 0) {
+      const uint32_t line = wave * A_LINES + j;
+      load_line_to_lds(ra, a_slot(w) + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+                       (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
+    } else {
+      const uint32_t line = wave * W_LINES + j;
+      load_line_to_lds(rw, w_slot(w) + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+                       (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
+    }
+  };
+  auto issue_loads = [&](int w) {
+#pragma unroll
+    for (int j = 0; j < A_LINES; ++j) issue_line(w, std::integral_constant<int, 0>{}, j);
+#pragma unroll
+    for (int j = 0; j < W_LINES; ++j) issue_line(w, std::integral_constant<int, 1>{}, j);
+  };
+  const int nchunks = (p.nwin + CW - 1) / CW;
+  auto issue_chunk = [&](int c) {
+    uint8_t* slot = lds + SC_BASE + (uint32_t)(c & 1) * SLOT;
+#pragma unroll
+    for (int j = 0; j < SC_LINES; ++j) {
+      const uint32_t line = wave * SC_LINES + j;
+      const bool is_w = line < BN / 32;
+      const uint32_t row0 = (is_w ? line : line - BN / 32) * 32;
+      load_line_to_lds(is_w ? rsw : rsa, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
+    }
+  };
+  auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
+  auto read_scales = [&](int w, uint32_t (&scw)[4], uint32_t (&sca)[2]) {
+    if constexpr (HAS_SC) {
+      const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
+      const uint32_t g = lane >> 5, r32 = lane & 31;
+      const uint32_t col = (uint32_t)(w % CW) * SC_WIN + ((SC_WIN == 8) ? 4 * g : 0);
+      const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * g;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        scw[i] = *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i + r32) * SC_ROW + col) >> sh;
+      if constexpr (MODE == GEMM_W4A4) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          sca[j] = *reinterpret_cast<const uint32_t*>(slot + (BN + wm * 64 + 32 * j + r32) * SC_ROW + col) >> sh;
+      }
+    }
+  };
+
+  v16f acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int nwin = p.nwin;
+  uint32_t scw[4] = {0, 0, 0, 0}, sca[2] = {0, 0};
+  v4i f0[8], f1[8];
+  constexpr int RD = (MODE == GEMM_W4A8) ? 8 : 6;        // ds_read_b128 per fragment set
+  constexpr int VM = A_LINES + W_LINES;
+  constexpr int VM1 = SPLIT ? A_LINES : W_LINES, VM0 = SPLIT ? W_LINES : A_LINES;
+  constexpr int WAIT_VM = SPLIT ? A_LINES : (NA - 2) * VM;
+
+  issue_loads(0);
+  if constexpr (HAS_SC) issue_chunk(0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if constexpr (HAS_SC)
+    if (nchunks > 1) issue_chunk(1);
+#pragma unroll
+  for (int k = 1; k < (SPLIT ? 2 : NS); ++k)
+    if (k < nwin) issue_loads(k);
+  read_frags8<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
+  read_scales(0, scw, sca);
+
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  auto window = [&](int w, auto pend_tag, auto steady_tag) {
+    constexpr bool PEND = decltype(pend_tag)::value;
+    constexpr bool STEADY = decltype(steady_tag)::value;
+    const uint8_t* la = a_slot(w);
+    const uint8_t* lw = w_slot(w);
+    if constexpr (HAS_SC)
+      if (chunk_due(w)) issue_chunk(w / CW + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    auto pend_loads = [&](int k) {
+      if constexpr (PEND) {
+        if (dma_after(k, VM1, RD) > 0) {
+          if constexpr (SPLIT)
+            issue_line(w + NA - 1, I0{}, k * VM1 / RD);
+          else
+            issue_line(w + NS - 1, I1{}, k * VM1 / RD);
+        }
+      }
+    };
+    uint32_t scw_n[4], sca_n[2];
+    if constexpr (C::STEPS == 4) {
+      read_frags8<MODE>(f1, la, lw, wm, wn, lane, 1, pend_loads);
+      mfma8<MODE, 0>(acc, f0, scw, sca);
+      interleave8<RD, PEND ? VM1 : 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags8<MODE>(f0, la, lw, wm, wn, lane, 2);
+      read_scales(w + 1, scw_n, sca_n);
+      mfma8<MODE, 1>(acc, f1, scw, sca);
+      interleave8<RD + (HAS_SC ? 4 : 0) + (MODE == GEMM_W4A4 ? 2 : 0), 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags8<MODE>(f1, la, lw, wm, wn, lane, 3);
+      mfma8<MODE, 2>(acc, f0, scw, sca);
+      interleave8<RD, 0>();
+    } else {
+      read_frags8<MODE>(f1, la, lw, wm, wn, lane, 1, pend_loads);
+      read_scales(w + 1, scw_n, sca_n);
+      mfma8<MODE, 0>(acc, f0, scw, sca);
+      interleave8<RD + (HAS_SC ? 4 : 0), PEND ? VM1 : 0>();
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (STEADY && WAIT_VM > 0)
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_VM));
+    else
+      __builtin_amdgcn_s_waitcnt(0);
+    stage_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    read_frags8<MODE>(f0, a_slot(w + 1), w_slot(w + 1), wm, wn, lane, 0, [&](int k) {
+      if constexpr (STEADY) {
+        if (dma_after(k, VM0, RD) > 0) {
+          if constexpr (SPLIT)
+            issue_line(w + NW, I1{}, k * VM0 / RD);
+          else
+            issue_line(w + NS, I0{}, k * VM0 / RD);
+        }
+      }
+    });
+    if constexpr (C::STEPS == 4)
+      mfma8<MODE, 3>(acc, f1, scw, sca);
+    else
+      mfma8<MODE, 1>(acc, f1, scw, sca);
+    interleave8<RD, STEADY ? VM0 : 0>();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) scw[i] = scw_n[i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sca[j] = sca_n[j];
+  };
+  using T_ = std::true_type;
+  using F_ = std::false_type;
+  int w = 0;
+  if constexpr (SPLIT) {
+    for (; w < nwin - 2; ++w) window(w, T_{}, T_{});
+  } else if (nwin > NS) {
+    window(0, F_{}, T_{});
+    for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{});
+    window(w, T_{}, F_{});
+    ++w;
+  }
+  for (; w < nwin; ++w) window(w, F_{}, F_{});
+
+  // ---- epilogue: fp32 -> bf16 (RNE) ----
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+  if (p.vec16 && n0 + BN <= p.N) {
+    // each wave parks its 64 x 128 sub-tile in its own 16 KB of LDS (16-byte chunk c of
+    // row r at slot c ^ (r & 15)) and stores 4 whole 256-byte row segments per instruction
+    __syncthreads();
+    uint8_t* sub = lds + wave * (64u * 256u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = 32 * j + r32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+          float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+          if constexpr (MODE == GEMM_W4A8) {
+            v0 *= p.a_scale;
+            v1 *= p.a_scale;
+            v2 *= p.a_scale;
+            v3 *= p.a_scale;
+          }
+          const uint32_t chunk = 4 * i + pp;
+          *reinterpret_cast<v2u*>(sub + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * g) =
+              v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+        }
+    }
+    const int mw = m0 + (int)wm * 64;
+    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
+      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
+      if (mw + (int)row < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)row * p.ld_out + c * 8) = v;
+    }
+    return;
+  }
+  const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + (int)(wm * 64 + 32 * j + r32);
+    uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
+        float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+        float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+        if constexpr (MODE == GEMM_W4A8) {
+          v0 *= p.a_scale;
+          v1 *= p.a_scale;
+          v2 *= p.a_scale;
+          v3 *= p.a_scale;
+        }
+        const unsigned lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
+        if (full) {
+          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+        } else if (m < p.M) {
+          if (p.vec_store && n + 4 <= p.N) {
+            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+          } else {
+            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
+            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
+            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
+            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Four blocks' worth of one lane's activations -> codes, with the block maxima reduced
+// across the quad by a transpose: the lanes of a quad hold 8 elements of each of four
+// blocks (their chunks i = 0..3); two DPP exchanges leave lane k with block k's maximum,
+// so each lane forms one scale (its own block's byte, returned in s) and broadcasts it
+// back to the quad for the conversion.  codes[i] = 4 code bytes of chunk i.
+template <bool UOS>
+__device__ __forceinline__ int mx_quad4_scale_bf16(const v4i (&d)[4], uint32_t lane, unsigned& s) {
+  unsigned m[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const unsigned x0 = (unsigned)d[i][0], x1 = (unsigned)d[i][1], x2 = (unsigned)d[i][2], x3 = (unsigned)d[i][3];
+    v2h mm = __builtin_elementwise_max(__builtin_bit_cast(v2h, x0 & 0x7FFF7FFFu), __builtin_bit_cast(v2h, x1 & 0x7FFF7FFFu));
+    mm = __builtin_elementwise_max(mm, __builtin_bit_cast(v2h, x2 & 0x7FFF7FFFu));
+    mm = __builtin_elementwise_max(mm, __builtin_bit_cast(v2h, x3 & 0x7FFF7FFFu));
+    m[i] = max((unsigned)mm[0], (unsigned)mm[1]);
+  }
+  const bool hi_pair = (lane & 2) != 0, odd = (lane & 1) != 0;
+  // exchange with lane ^ 2: keep blocks {2p, 2p+1} (p = lane bit 1), send the other pair
+  const unsigned snd0 = hi_pair ? m[0] : m[2], snd1 = hi_pair ? m[1] : m[3];
+  const unsigned kp0 = hi_pair ? m[2] : m[0], kp1 = hi_pair ? m[3] : m[1];
+  const unsigned t0 = max(kp0, (unsigned)__builtin_amdgcn_mov_dpp((int)snd0, 0x4E, 0xF, 0xF, true));
+  const unsigned t1 = max(kp1, (unsigned)__builtin_amdgcn_mov_dpp((int)snd1, 0x4E, 0xF, 0xF, true));
+  // exchange with lane ^ 1: keep block 2p + (lane bit 0)
+  const unsigned snd = odd ? t0 : t1, kp = odd ? t1 : t0;
+  const unsigned amax = max(kp, (unsigned)__builtin_amdgcn_mov_dpp((int)snd, 0xB1, 0xF, 0xF, true));
+  const unsigned e = amax >> 7;
+  if constexpr (UOS) {
+    s = scale_byte_uos(e, (amax & 0x7Fu) > 0x68u ? 1u : 0u);
+  } else {
+    const unsigned t = __builtin_elementwise_sub_sat(e, 2u);
+    s = e == 255u ? 255u : t;
+  }
+  return (int)max(s << 23, 0x00400000u);
+}
+
+// The conversion half of the above: scale_bits = this lane's block scale (binary32 bits).
+__device__ __forceinline__ void mx_quad4_convert_bf16(const v4i (&d)[4], int scale_bits, unsigned (&codes)[4]) {
+  auto convert = [&](auto i_tag) {
+    constexpr int I = decltype(i_tag)::value;
+    // block I's scale lives in lane I of the quad: quad_perm [I, I, I, I]
+    const float sc = __int_as_float(__builtin_amdgcn_mov_dpp(scale_bits, I * 0x55, 0xF, 0xF, true));
+    const unsigned x0 = (unsigned)d[I][0], x1 = (unsigned)d[I][1], x2 = (unsigned)d[I][2], x3 = (unsigned)d[I][3];
+    unsigned r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(x0, __builtin_bit_cast(bf16x2, x0), sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x1), sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x2), sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, x3), sc, 3);
+    codes[I] = r;
+  };
+  convert(std::integral_constant<int, 0>{});
+  convert(std::integral_constant<int, 1>{});
+  convert(std::integral_constant<int, 2>{});
+  convert(std::integral_constant<int, 3>{});
+}
+
 // Fast fused kernel (bf16 activations; K a whole number of 256-element windows; weight
-// scale rows and planes on 16-byte boundaries).  Weights and their scale chunks stream as
-// in gemm_fast_kernel<GEMM_W4A4> (two-slot weight ring, 32-byte scale chunks).  The
-// activation window w+1 is quantized during window w, a quarter per MFMA step: wave v
-// quantizes rows 64v + 16q .. +15 of quarter q, loaded into registers D steps earlier
-// (1 KB = 2 rows x 256 elements per load instruction), and writes 4 code bytes per lane
-// into the two-slot code ring and the block scale into a two-slot scale plane (lanes
-// that do not own a block's scale write into a sink beside it, so no lane branches).
-// Quarter 0 of window w+1 is quantized after the hand-over barrier of window w-1, which
-// releases its slot; quarters 1-3 under steps 0-2 of window w.
-//
-// Each MFMA step is issued as four units in source order, fenced from each other: 4
-// MFMAs, 2 fragment reads for the next step, 2 blocks quantized and stored, 2 activation
-// loads (and under the last step 2 weight-tile lines and a scale read).  The matrix core
-// works through a unit's MFMAs while the wave issues the unit's vector work.
+// scale rows and planes on 16-byte boundaries), eight waves: the MFMA layout and weight
+// streaming of gemm_fast8_kernel<GEMM_W4A4> (wave = 64 x 128 sub-tile; two-slot weight
+// ring; 32-byte weight scale chunks), and the activation tile quantized in the kernel.
+// Activation window w+1 is quantized during window w, a quarter per MFMA step: wave v
+// quantizes rows 32v + 8q .. +7 of quarter q from registers loaded D steps earlier (1 KB =
+// 2 rows x 256 elements per load instruction, 4 per quarter), and writes 4 code bytes per
+// chunk into the two-slot code ring (the swizzled layout the W4A4 kernels stage) and its
+// block's scale byte into a two-slot [256 x 8] plane.  Quarter 0 of window w+1 is
+// quantized after the hand-over barrier of window w-1, which releases its slot; quarters
+// 1-3 under steps 0-2 of window w.  A step runs as two units in source order, fenced
+// from each other: 4 MFMAs, 3 fragment reads and half of the quantization each.
 template <bool UOS, int D>
-__global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
-  static_assert(D == 2 || D == 4, "load lead of 2 or 4 steps");
+__global__ __launch_bounds__(NT8, 1) void gemm_w4a4_fused8_kernel(Params p) {
+  static_assert(D == 1 || D == 2 || D == 4, "load lead of 1, 2 or 4 steps");
+  constexpr int WAVES = NT8 / 64;
   constexpr uint32_t A_TILE = BM * 128, W_TILE = BN * 128;   // code tiles, 32 KB each
-  constexpr int W_LINES = (int)(W_TILE / 1024 / 4);           // 1 KB weight lines per wave per window
-  static_assert(W_LINES == 8, "two weight lines per unit");
+  constexpr int W_LINES = (int)(W_TILE / 1024 / WAVES);       // 4 weight lines per wave per window
   constexpr uint32_t W_BASE = 2 * A_TILE;
   constexpr uint32_t SC_ROW = 32;                             // weight scale chunk: 32 bytes per row
   constexpr int CW = 4;                                       // windows per chunk
   constexpr uint32_t SLOT = BN * SC_ROW;
-  constexpr int SC_LINES = (int)(SLOT / 1024 / 4);
+  constexpr int SC_LINES = (int)(SLOT / 1024 / WAVES);        // 1
   constexpr uint32_t SC_BASE = W_BASE + 2 * W_TILE;
   constexpr uint32_t AS_BASE = SC_BASE + 2 * SLOT;
-  constexpr uint32_t AS_SLOT = 4096;                          // [256 rows][8] scale bytes + 2 KB sink
+  constexpr uint32_t AS_SLOT = BM * 8;                        // [256 rows][8] scale bytes
   __shared__ __attribute__((aligned(1024))) uint8_t lds[AS_BASE + 2 * AS_SLOT];
+  static_assert(AS_BASE + 2 * AS_SLOT >= 8u * 16384u, "epilogue staging fits");
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
-  const uint32_t wm = wave & 1, wn = wave >> 1;
+  const uint32_t wm = wave & 3, wn = wave >> 2;
   int m0, n0;
   tile_origin(p, m0, n0);
   const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
@@ -1104,19 +1528,16 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
   const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w_scales + (int64_t)n0 * p.scale_row_bytes, rows_w * p.scale_row_bytes);
   const uint32_t pitch = p.a_row_bytes;
 
-  // weight tile lines: 128-byte rows, 8 per 1 KB line; lane i lands at slot i % 8 of row
-  // i / 8 and fetches the chunk the swizzle puts there (even / odd lines differ)
   const uint32_t wr = lane >> 3, wsl = lane & 7;
   const uint32_t w_voff0 = wr * p.w_row_bytes + ((wsl ^ ((wr >> 1) & 7u)) * 16);
   const uint32_t w_voff1 = wr * p.w_row_bytes + ((wsl ^ (((8u + wr) >> 1) & 7u)) * 16);
   const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
-  // activation loads and code / scale writes: load i of a quarter covers rows 2i, 2i+1
-  // (lane / 32) of the wave's 16, elements 8 (lane % 32) ..; the code slot of row r,
-  // block b is b ^ ((r >> 1) & 7) = b ^ i
+  // load i of quarter q covers rows 32v + 8q + 2i + (lane / 32), elements 8 (lane % 32) ..
+  // of the window; the code slot of row r, block b is b ^ ((r >> 1) & 7) = b ^ (4 (q & 1) + i)
   const uint32_t h = lane >> 5, b = (lane & 31) >> 2, k = lane & 3;
   const uint32_t a_voff = h * pitch + 16 * (lane & 31);
-  const uint32_t cw0 = wave * 8192u + h * 128u + 4u * k + (b << 4);
-  const uint32_t sw0 = k == 0 ? wave * 512u + h * 8u + b : 2048u + lane;
+  const uint32_t cw0 = wave * 4096u + h * 128u + 4u * k + (b << 4);
+  const uint32_t sw0 = (wave * 32u + 2u * k + h) * 8u + b;     // scale byte of the quad's block k
 
   auto issue_w_line = [&](int w, int par, int j) {
     const uint32_t line = wave * W_LINES + j;
@@ -1133,8 +1554,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
       load_line_to_lds(rsw, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + line * 32 * p.scale_row_bytes);
     }
   };
-  // chunk c+1 goes out at the start of window c*CW (c >= 1): every wave has passed its
-  // last read of chunk c-1, the slot's previous occupant
   auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
   auto read_w_scale = [&](int w, uint32_t ln, int i) {
     const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
@@ -1143,33 +1562,43 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
   };
   auto read_a_scale = [&](int par, uint32_t ln, int j) {
     return *reinterpret_cast<const uint32_t*>(lds + AS_BASE + (uint32_t)par * AS_SLOT +
-                                              (wm * 128 + 32 * j + (ln & 31)) * 8 + 4 * (ln >> 5));
+                                              (wm * 64 + 32 * j + (ln & 31)) * 8 + 4 * (ln >> 5));
   };
-  // fragment kk (0-3: weight rows, 4-7: activation rows) of MFMA step t from slot `par`
+  // fragment kk (0-3: weight rows wn*128 + 32kk, 4-5: activation rows wm*64 + 32(kk-4)) of
+  // MFMA step t from slot `par`
   auto read_frag = [&](int par, uint32_t ln, int t, int kk) {
     const uint32_t chunk = (ln >> 5) * 4 + t;
     const uint8_t* base = kk < 4 ? lds + W_BASE + (uint32_t)par * W_TILE : lds + (uint32_t)par * A_TILE;
-    const uint32_t row = (kk < 4 ? wn : wm) * 128 + 32 * (kk & 3) + (ln & 31);
+    const uint32_t row = kk < 4 ? wn * 128 + 32 * kk + (ln & 31) : wm * 64 + 32 * (kk - 4) + (ln & 31);
     return *reinterpret_cast<const v4i*>(base + swz128(row, chunk));
   };
-  // load i of quarter q of activation window v
   auto load_act = [&](int v, int q, int i) {
-    return __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, (uint32_t)(64 * wave + 16 * q + 2 * i) * pitch + (uint32_t)v * 512u,
+    return __builtin_amdgcn_raw_buffer_load_b128(ra, a_voff, (uint32_t)(32 * wave + 8 * q + 2 * i) * pitch + (uint32_t)v * 512u,
                                                  0);
   };
-  // quantize load i of quarter q into code / scale slot `par`
-  auto quant_act = [&](int par, int q, int i, v4i d) {
+  // quantize quarter q (4 loads) into code / scale slot `par`: the block scales (and the
+  // scale bytes), then the codes
+  auto quant_scale = [&](int par, int q, const v4i (&d)[4]) {
     unsigned s;
-    const unsigned c = mx_quant8_bf16<UOS>(d, s);
-    *reinterpret_cast<unsigned*>(lds + (uint32_t)par * A_TILE + q * 2048 + 256 * i + (cw0 ^ ((uint32_t)i << 4))) = c;
-    lds[AS_BASE + (uint32_t)par * AS_SLOT + q * 128 + 16 * i + sw0] = (uint8_t)s;
+    const int bits = mx_quad4_scale_bf16<UOS>(d, lane, s);
+    lds[AS_BASE + (uint32_t)par * AS_SLOT + q * 64 + sw0] = (uint8_t)s;
+    return bits;
   };
+  auto quant_codes = [&](int par, int q, const v4i (&d)[4], int bits) {
+    unsigned c[4];
+    mx_quad4_convert_bf16(d, bits, c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<unsigned*>(lds + (uint32_t)par * A_TILE + q * 1024 + 256 * i +
+                                   (cw0 ^ ((uint32_t)(4 * (q & 1) + i) << 4))) = c[i];
+  };
+  auto quant_quarter = [&](int par, int q, const v4i (&d)[4]) { quant_codes(par, q, d, quant_scale(par, q, d)); };
 
-  v16f acc[4][4];
+  v16f acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
@@ -1183,47 +1612,44 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
   issue_chunk(0);
 #pragma unroll
   for (int Q = 0; Q < 5; ++Q) {
-    v4i d[8];
+    v4i d[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) d[i] = load_act(Q / 4, Q % 4, i);
-    if (Q / 4 < nwin) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) quant_act((Q / 4) & 1, Q % 4, i, d[i]);
-    }
+    for (int i = 0; i < 4; ++i) d[i] = load_act(Q / 4, Q % 4, i);
+    if (Q / 4 < nwin) quant_quarter((Q / 4) & 1, Q % 4, d);
     __builtin_amdgcn_sched_barrier(0);
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   issue_chunk(1);
-  v4i stg[D][8];
+  v4i stg[D][4];
 #pragma unroll
   for (int Q = 5; Q < 5 + D; ++Q)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) stg[(Q % 4) % D][i] = load_act(Q / 4, Q % 4, i);
+    for (int i = 0; i < 4; ++i) stg[(Q % 4) % D][i] = load_act(Q / 4, Q % 4, i);
 #pragma unroll
   for (int j = 0; j < W_LINES; ++j) issue_w_line(1, 1, j);
-  uint32_t scw[4], sca[4];
-  v4i f0[8], f1[8];
+  uint32_t scw[4], sca[2];
+  v4i f0[6], f1[6];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) f0[kk] = read_frag(0, lane, 0, kk);
+  for (int kk = 0; kk < 6; ++kk) f0[kk] = read_frag(0, lane, 0, kk);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    scw[i] = read_w_scale(0, lane, i);
-    sca[i] = read_a_scale(0, lane, i);
-  }
+  for (int i = 0; i < 4; ++i) scw[i] = read_w_scale(0, lane, i);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) sca[j] = read_a_scale(0, lane, j);
 
-  // One window w with slot parity PAR = w & 1 (a constant in the steady state).  Region r (the MFMAs of step r) quantizes
-  // global quarter 4w + r + 5 (window w+1 quarters 1..3, then window w+2 quarter 0) from
-  // the registers loaded D regions earlier and loads quarter 4w + r + 5 + D into them.
-  // TAIL windows check each against the window count and drain all loads at the hand-over.
+  // One window w with slot parity PAR = w & 1 (a constant in the steady state).  Region r
+  // (the MFMAs of step r) quantizes global quarter 4w + r + 5 (window w+1 quarters 1..3,
+  // then window w+2 quarter 0) from the registers loaded D regions earlier and loads
+  // quarter 4w + r + 5 + D into them.  TAIL windows check each against the window count
+  // and drain all loads at the hand-over.
   auto window = [&](int w, int PAR, auto tail_tag) {
     constexpr bool TAIL = decltype(tail_tag)::value;
     uint32_t ln = lane;
     asm volatile("" : "+v"(ln));
     if (chunk_due(w)) issue_chunk(w / CW + 1);
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t scw_n[4], sca_n[4];
-    auto region = [&](auto r_tag, v4i (&fc)[8], v4i (&fn)[8]) {
+    uint32_t scw_n[4], sca_n[2];
+    auto region = [&](auto r_tag, v4i (&fc)[6], v4i (&fn)[6]) {
       constexpr int R = decltype(r_tag)::value;
       constexpr int QC = (R + 1) & 3, VC = (R + 5) >> 2;           // quarter quantized: window w + VC
       constexpr int QL = (R + 1 + D) & 3, VL = (R + 5 + D) >> 2;   // quarter loaded: window w + VL
@@ -1232,30 +1658,43 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
       const int PC = (PAR + VC) & 1;                               // code / scale slot quantized into
       const bool q_ok = !TAIL || w + VC < nwin;
       const bool l_ok = !TAIL || w + VL < nwin;
+      int bits = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 2; ++u) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[u][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fc[u]), widen(fc[4 + j]), acc[u][j], 4, 4,
-                                                                      R, (int)scw[u], R, (int)sca[j]);
-        if constexpr (R < 3) {
-          fn[2 * u] = read_frag(PAR, ln, R + 1, 2 * u);
-          fn[2 * u + 1] = read_frag(PAR, ln, R + 1, 2 * u + 1);
-          if constexpr (R == 1) scw_n[u] = read_w_scale(w + 1, ln, u);
-        } else {
-          fn[2 * u] = read_frag(PAR ^ 1, ln, 0, 2 * u);
-          if (!TAIL || w + 2 < nwin) issue_w_line(w + 2, PAR, 2 * u);
-          fn[2 * u + 1] = read_frag(PAR ^ 1, ln, 0, 2 * u + 1);
-          if (!TAIL || w + 2 < nwin) issue_w_line(w + 2, PAR, 2 * u + 1);
+        for (int i = 2 * u; i < 2 * u + 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(fc[i]), widen(fc[4 + j]), acc[i][j], 4, 4,
+                                                                        R, (int)scw[i], R, (int)sca[j]);
+#pragma unroll
+        for (int kk = 3 * u; kk < 3 * u + 3; ++kk) {
+          if constexpr (R < 3) {
+            fn[kk] = read_frag(PAR, ln, R + 1, kk);
+          } else {
+            fn[kk] = read_frag(PAR ^ 1, ln, 0, kk);
+            if (kk < W_LINES && (!TAIL || w + 2 < nwin)) issue_w_line(w + 2, PAR, kk);
+          }
+        }
+        if constexpr (R == 1) {
+          scw_n[2 * u] = read_w_scale(w + 1, ln, 2 * u);
+          scw_n[2 * u + 1] = read_w_scale(w + 1, ln, 2 * u + 1);
+        }
+        if constexpr (R == 3) {
+          if (u == 1 && (!TAIL || w + 2 < nwin)) issue_w_line(w + 2, PAR, 3);
           sca_n[u] = read_a_scale(PAR ^ 1, ln, u);
         }
-        if (q_ok) {
-          quant_act(PC, QC, 2 * u, stg[IX][2 * u]);
-          quant_act(PC, QC, 2 * u + 1, stg[IX][2 * u + 1]);
-        }
-        if (l_ok) {
-          stg[IX][2 * u] = load_act(w + VL, QL, 2 * u);
-          stg[IX][2 * u + 1] = load_act(w + VL, QL, 2 * u + 1);
+        // unit 0: block scales of the quarter; unit 1: its codes, then (after a fence, so
+        // that they reuse the registers just read) the loads of the next quarter
+        if (u == 0) {
+          if (q_ok) bits = quant_scale(PC, QC, stg[IX]);
+        } else {
+          if (q_ok) quant_codes(PC, QC, stg[IX], bits);
+          __builtin_amdgcn_sched_barrier(0);
+          if (l_ok) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) stg[IX][i] = load_act(w + VL, QL, i);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -1263,23 +1702,22 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
     region(std::integral_constant<int, 0>{}, f0, f1);
     region(std::integral_constant<int, 1>{}, f1, f0);
     region(std::integral_constant<int, 2>{}, f0, f1);
-    // hand-over: weight window w+1 landed (at least 16 activation loads went out after
-    // it), this wave's code and scale writes for window w+1 done; then every wave is past
-    // its reads of window w's slots
+    // hand-over: weight window w+1 landed (at least 16 loads went out after it), this
+    // wave's code and scale writes for window w+1 done; then every wave is past its reads
+    // of window w's slots
     if constexpr (TAIL)
       __builtin_amdgcn_s_waitcnt(0);
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(4 * (D < 3 ? D : 3)));
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
     region(std::integral_constant<int, 3>{}, f1, f0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      scw[i] = scw_n[i];
-      sca[i] = sca_n[i];
-    }
+    for (int i = 0; i < 4; ++i) scw[i] = scw_n[i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sca[j] = sca_n[j];
   };
-  constexpr int TAIL_WINDOWS = D == 2 ? 2 : 3;
+  constexpr int TAIL_WINDOWS = D <= 2 ? 2 : 3;
   const int steady = nwin - TAIL_WINDOWS;
   int w = 0;
   for (; w + 1 < steady; w += 2) {
@@ -1292,7 +1730,61 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_kernel(Params p) {
   }
   for (; w < nwin; ++w) window(w, w & 1, std::true_type{});
 
-  store_tile_w4a4(p, acc, lds, wave, lane, wm, wn, m0, n0);
+  // ---- epilogue: fp32 -> bf16 (RNE), staged per wave through 16 KB of LDS ----
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+  if (p.vec16 && n0 + BN <= p.N) {
+    __syncthreads();
+    uint8_t* sub = lds + wave * (64u * 256u);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t row = 32 * j + r32;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int pp = 0; pp < 4; ++pp) {
+          const uint32_t chunk = 4 * i + pp;
+          *reinterpret_cast<v2u*>(sub + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * g) =
+              v2u{pack_bf16x2(acc[i][j][4 * pp + 0], acc[i][j][4 * pp + 1]),
+                  pack_bf16x2(acc[i][j][4 * pp + 2], acc[i][j][4 * pp + 3])};
+        }
+    }
+    const int mw = m0 + (int)wm * 64;
+    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
+      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
+      if (mw + (int)row < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)row * p.ld_out + c * 8) = v;
+    }
+    return;
+  }
+  const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int m = m0 + (int)(wm * 64 + 32 * j + r32);
+    uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
+        const unsigned lo = pack_bf16x2(acc[i][j][4 * pp + 0], acc[i][j][4 * pp + 1]);
+        const unsigned hi = pack_bf16x2(acc[i][j][4 * pp + 2], acc[i][j][4 * pp + 3]);
+        if (full) {
+          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+        } else if (m < p.M) {
+          if (p.vec_store && n + 4 <= p.N) {
+            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+          } else {
+            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
+            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
+            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
+            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
+          }
+        }
+      }
+    }
+  }
 }
 
 }  // namespace
@@ -1328,7 +1820,13 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
     p.w_row_bytes = w_row_bytes;
     if (K > 0 && K % Fast<MD>::K_WIN == 0 && (scales_ok || !needs_scales)) {
       p.nwin = (int)(K / Fast<MD>::K_WIN);
-      hipLaunchKernelGGL(gemm_fast_kernel<MD>, grid, block, 0, stream, p);
+      // the bf16 reference runs two waves per SIMD (measured faster); the scaled modes one
+      // (with the 64 x 128 wave tile their fragment reads per MFMA grow by half and the
+      // LDS becomes the limit)
+      if constexpr (MD == GEMM_BF16)
+        hipLaunchKernelGGL(gemm_fast8_kernel<MD>, grid, dim3(NT8), 0, stream, p);
+      else
+        hipLaunchKernelGGL(gemm_fast_kernel<MD>, grid, block, 0, stream, p);
     } else {
       p.nwin = (int)((K + Cfg<MD>::K_WIN - 1) / Cfg<MD>::K_WIN);
       hipLaunchKernelGGL(gemm_generic_kernel<MD>, grid, block, 0, stream, p);
@@ -1377,9 +1875,9 @@ hipError_t launch_gemm_w4a4_fused(const void* a, bool f32, int64_t ld_a, const u
   if (fast) {
     p.nwin = (int)(K / 256);
     if (uos)
-      hipLaunchKernelGGL((gemm_w4a4_fused_kernel<true, 2>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((gemm_w4a4_fused8_kernel<true, 2>), grid, dim3(NT8), 0, stream, p);
     else
-      hipLaunchKernelGGL((gemm_w4a4_fused_kernel<false, 2>), grid, block, 0, stream, p);
+      hipLaunchKernelGGL((gemm_w4a4_fused8_kernel<false, 2>), grid, dim3(NT8), 0, stream, p);
   } else {
     p.nwin = (int)((K + 255) / 256);
     if (f32) {
