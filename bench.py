@@ -271,8 +271,17 @@ def main():
                                      "peak": PEAK["fp4_TFLOPs"], "frac": round(rate_f / PEAK["fp4_TFLOPs"], 4)},
              "quantize_plus_w4a4_ms": round(per_kernel_ms["mxq_quantize"] + per_kernel_ms["mxq_gemm_w4a4"], 4),
              "bit_identical_to_quantize_then_w4a4": fused_same}
+    # MXFP4 -> bf16 dequantization (the QDQ step) of the activation codes, into a bf16 buffer
+    mxq.quantize_into(a, ac, asc)
+    y_dq = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    ms_dq = time_fn(lambda: mxq.dequantize(ac, asc, K, out=y_dq))
+    del y_dq
+    dq_rate = M * K * (0.5 + 1 / 32 + 2) / (ms_dq * 1e-3) / 1e9
+    dequant = {"mxq_dequantize": {"ms": round(ms_dq, 4), "achieved": round(dq_rate, 2), "unit": "GB/s",
+                                  "peak": PEAK["hbm_GBps"], "frac": round(dq_rate / PEAK["hbm_GBps"], 4)}}
     res["next"] = {
         "fused_activation_quant": fused,
+        "dequantize": dequant,
         "hadamard_rotation": hada,
         "uos_scale_rule": {
             "mxq_quantize_uos": {"ms": round(ms_uos, 4), "achieved": round(q_amount / (ms_uos * 1e-3) / 1e9, 2),

@@ -278,11 +278,16 @@ def sqnr(ref, test, workspace=None, out3=None) -> torch.Tensor:
     return out3
 
 
-def dequantize(codes, scales, K: int) -> torch.Tensor:
-    """MXFP4 -> bf16 [R, K]."""
+def dequantize(codes, scales, K: int, out=None) -> torch.Tensor:
+    """MXFP4 -> bf16 [R, K] (into ``out`` if given: bfloat16 [R, K], rows may be strided)."""
     _dev(codes, "codes")
     R = codes.shape[0]
-    y = torch.empty((R, K), dtype=torch.bfloat16, device=codes.device)
+    if out is None:
+        y, ld = torch.empty((R, K), dtype=torch.bfloat16, device=codes.device), K
+    else:
+        if out.dtype != torch.bfloat16 or out.shape != (R, K):
+            raise ValueError("out must be bfloat16 [R, K]")
+        y, ld = out, _rowmajor(out, "out")
     _check(lib.mxq_dequantize(_p(codes), _rowmajor(codes, "codes"), _p(scales), _rowmajor(scales, "scales"),
-                              R, K, _p(y), K, _stream()))
+                              R, K, _p(y), ld, _stream()))
     return y

@@ -39,6 +39,11 @@ constexpr int kMxThreads = 512;
 constexpr int kMxUnroll = 8;
 constexpr int kMxBlocksPerIter = kMxThreads / 4 * kMxUnroll;
 constexpr int kFp8Threads = 1024;
+constexpr int kFp8Unroll = 2;     // chunks of 16 per lane per pass (72 % of HBM against 69 % for one)
+// dequantize_kernel: 8 quarter-blocks per lane per pass in 512-thread workgroups (71 % of
+// HBM against 58 % for one quarter per lane and 256 threads)
+constexpr int kDqThreads = 512;
+constexpr int kDqUnroll = 8;
 
 __device__ __forceinline__ float lo_f32(int pair) { return __uint_as_float((unsigned)pair << 16); }
 __device__ __forceinline__ float hi_f32(int pair) { return __uint_as_float((unsigned)pair & 0xFFFF0000u); }
@@ -275,52 +280,71 @@ template <bool F32>
 __global__ __launch_bounds__(kFp8Threads) void fp8_quantize_kernel(
     const void* __restrict__ x, int64_t ld_x, float inv_scale, uint8_t* __restrict__ out, int64_t ld_q,
     uint32_t chunks_per_row, int64_t total_chunks, int contiguous) {
-  const int64_t stride = (int64_t)gridDim.x * kFp8Threads;
-  for (int64_t c = (int64_t)blockIdx.x * kFp8Threads + threadIdx.x; c < total_chunks; c += stride) {
-    int64_t xo, qo;
-    if (contiguous) {
-      xo = c * 16;
-      qo = c * 16;
-    } else {
-      const uint32_t cc = (uint32_t)c;
-      const uint32_t row = cc / chunks_per_row;
-      const uint32_t col = cc - row * chunks_per_row;
-      xo = (int64_t)row * ld_x + col * 16;
-      qo = (int64_t)row * ld_q + col * 16;
-    }
-    float v[16];
-    if (F32) {
-      const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
+  // each lane takes kFp8Unroll chunks of 16 elements per pass, loads first
+  const int64_t stride = (int64_t)gridDim.x * kFp8Threads * kFp8Unroll;
+  for (int64_t c0 = (int64_t)blockIdx.x * kFp8Threads * kFp8Unroll + threadIdx.x; c0 < total_chunks; c0 += stride) {
+    v4i d[kFp8Unroll][4];
+    int64_t qo[kFp8Unroll];
+    bool ok[kFp8Unroll];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const v4i d = __builtin_nontemporal_load(p + i);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[4 * i + j] = __int_as_float(d[j]);
+    for (int u = 0; u < kFp8Unroll; ++u) {
+      const int64_t c = c0 + (int64_t)u * kFp8Threads;
+      ok[u] = c < total_chunks;
+      int64_t xo;
+      if (contiguous) {
+        xo = c * 16;
+        qo[u] = c * 16;
+      } else {
+        const uint32_t cc = (uint32_t)c;
+        const uint32_t row = cc / chunks_per_row;
+        const uint32_t col = cc - row * chunks_per_row;
+        xo = (int64_t)row * ld_x + col * 16;
+        qo[u] = (int64_t)row * ld_q + col * 16;
       }
-    } else {
-      const v4i* p = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const v4i d = __builtin_nontemporal_load(p + i);
+      for (int i = 0; i < 4; ++i) d[u][i] = v4i{0, 0, 0, 0};
+      if (ok[u]) {
+        if (F32) {
+          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[8 * i + 2 * j] = __uint_as_float((unsigned)d[j] << 16);
-          v[8 * i + 2 * j + 1] = __uint_as_float((unsigned)d[j] & 0xFFFF0000u);
+          for (int i = 0; i < 4; ++i) d[u][i] = __builtin_nontemporal_load(p + i);
+        } else {
+          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo);
+          d[u][0] = __builtin_nontemporal_load(p);
+          d[u][1] = __builtin_nontemporal_load(p + 1);
         }
       }
     }
-    v4i o;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float y[4];
+    for (int u = 0; u < kFp8Unroll; ++u) {
+      float v[16];
+      if (F32) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) y[j] = __builtin_amdgcn_fmed3f(v[4 * i + j] * inv_scale, -448.0f, 448.0f);
-      int r = 0;
-      r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], r, false);
-      r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
-      o[i] = r;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) v[4 * i + jj] = __int_as_float(d[u][i][jj]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            v[8 * i + 2 * jj] = __uint_as_float((unsigned)d[u][i][jj] << 16);
+            v[8 * i + 2 * jj + 1] = __uint_as_float((unsigned)d[u][i][jj] & 0xFFFF0000u);
+          }
+      }
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float y[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) y[jj] = __builtin_amdgcn_fmed3f(v[4 * i + jj] * inv_scale, -448.0f, 448.0f);
+        int r = 0;
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], r, false);
+        r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
+        o[i] = r;
+      }
+      if (ok[u]) __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(out + qo[u]));
     }
-    __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(out + qo));
   }
 }
 
@@ -372,34 +396,49 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* __restrict
 // MXFP4 -> bf16: e2m1(code) * 2^(s - 127).  The product is formed in binary32 (exact:
 // at most 3 significant bits, exponent within binary32's range down to the subnormal
 // 2^-128) and narrowed to bf16 with round to nearest even (exact in range).
-__global__ __launch_bounds__(kThreads) void dequantize_kernel(
+__global__ __launch_bounds__(kDqThreads) void dequantize_kernel(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
     int64_t ld_scales, uint16_t* __restrict__ y, int64_t ld_y, uint32_t blocks_per_row,
     int64_t total_quarters) {
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t g = (int64_t)blockIdx.x * kThreads + threadIdx.x; g < total_quarters; g += stride) {
-    const int64_t b = g >> 2;
-    const int q = (int)(g & 3);
-    const uint32_t row = (uint32_t)(b / blocks_per_row);
-    const uint32_t blk = (uint32_t)(b - (int64_t)row * blocks_per_row);
-    const unsigned c = *reinterpret_cast<const unsigned*>(codes + (int64_t)row * ld_codes + blk * 16 + q * 4);
-    const unsigned s = scales[(int64_t)row * ld_scales + blk];
-    // 2 * |e2m1| for magnitude codes 0..7 is 0,1,2,3,4,6,8,12: one nibble each
-    const float half_scale = s >= 2 ? __uint_as_float((s - 1) << 23) : (s == 1 ? 0x1p-127f : 0x1p-128f);
-    const float sc = s == 255 ? __uint_as_float(0x7FC00000u) : half_scale;
-    v4i o;
+  // each lane takes kDqUnroll quarters (8 elements each) per pass, loads first
+  const int64_t stride = (int64_t)gridDim.x * kDqThreads * kDqUnroll;
+  for (int64_t g0 = (int64_t)blockIdx.x * kDqThreads * kDqUnroll + threadIdx.x; g0 < total_quarters; g0 += stride) {
+    unsigned c[kDqUnroll], s[kDqUnroll];
+    int64_t yo[kDqUnroll];
+    bool ok[kDqUnroll];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      float f[2];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const unsigned code = (c >> (8 * i + 4 * h)) & 0xF;
-        const float mag = (float)((0xC8643210u >> (4 * (code & 7))) & 0xF) * sc;
-        f[h] = (code & 8) ? -mag : mag;
-      }
-      o[i] = (int)pack_bf16x2(f[0], f[1]);
+    for (int u = 0; u < kDqUnroll; ++u) {
+      const int64_t g = g0 + (int64_t)u * kDqThreads;
+      ok[u] = g < total_quarters;
+      const int64_t b = g >> 2;
+      const int q = (int)(g & 3);
+      const uint32_t row = (uint32_t)(b / blocks_per_row);
+      const uint32_t blk = (uint32_t)(b - (int64_t)row * blocks_per_row);
+      c[u] = ok[u] ? *reinterpret_cast<const unsigned*>(codes + (int64_t)row * ld_codes + blk * 16 + q * 4) : 0u;
+      s[u] = ok[u] ? scales[(int64_t)row * ld_scales + blk] : 0u;
+      yo[u] = (int64_t)row * ld_y + blk * 32 + q * 8;
     }
-    *reinterpret_cast<v4i*>(y + (int64_t)row * ld_y + blk * 32 + q * 8) = o;
+#pragma unroll
+    for (int u = 0; u < kDqUnroll; ++u) {
+      // 2 * |e2m1| for magnitude codes 0..7 is 0,1,2,3,4,6,8,12: one nibble each
+      const unsigned sv = s[u];
+      const float half_scale = sv >= 2 ? __uint_as_float((sv - 1) << 23) : (sv == 1 ? 0x1p-127f : 0x1p-128f);
+      const float sc = sv == 255 ? __uint_as_float(0x7FC00000u) : half_scale;
+      v4i o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float f[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const unsigned code = (c[u] >> (8 * i + 4 * h)) & 0xF;
+          const float mag = (float)((0xC8643210u >> (4 * (code & 7))) & 0xF) * sc;
+          f[h] = (code & 8) ? -mag : mag;
+        }
+        o[i] = (int)pack_bf16x2(f[0], f[1]);
+      }
+      // the output is not read again here: stream it past the caches
+      if (ok[u]) __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(y + yo[u]));
+    }
   }
 }
 
@@ -469,7 +508,7 @@ hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t co
   const int64_t total = rows * cpr;
   if (total == 0) return hipSuccess;
   const int contiguous = (ld_x == cols && ld_q == cols) ? 1 : 0;
-  const int grid = grid_for(total, kFp8Threads);
+  const int grid = grid_for(total, kFp8Threads * kFp8Unroll);
   if (f32)
     hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3(grid), dim3(kFp8Threads), 0, stream, x, ld_x, inv_scale,
                        q, ld_q, (uint32_t)cpr, total, contiguous);
@@ -503,8 +542,8 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8
   const int64_t bpr = cols / 32;
   const int64_t total = rows * bpr * 4;
   if (total == 0) return hipSuccess;
-  const int grid = grid_for(total, kThreads);
-  hipLaunchKernelGGL(dequantize_kernel, dim3(grid), dim3(kThreads), 0, stream, codes, ld_codes, scales,
+  const int grid = grid_for(total, kDqThreads * kDqUnroll);
+  hipLaunchKernelGGL(dequantize_kernel, dim3(grid), dim3(kDqThreads), 0, stream, codes, ld_codes, scales,
                      ld_scales, y, ld_y, (uint32_t)bpr, total);
   return hipGetLastError();
 }

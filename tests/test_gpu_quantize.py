@@ -203,3 +203,20 @@ def test_dequantize_every_code_and_scale(gpu):
     ref_bits = oracle.f64_to_bf16_bits(np.where(finite, ref, 0.0))
     got = to_np_bf16_bits(y)
     np.testing.assert_array_equal(got[finite], ref_bits[finite])
+
+
+def test_dequantize_workload_rows_and_strided_output(gpu):
+    name = "wan_ffn_down_sqnr"
+    wl = workloads.WORKLOADS[name]
+    a = workloads.activations(2048, wl.K, wl.act, seed=0, name=name, device="cpu")
+    rc, rs = oracle.quantize_mxfp4(bf16_bits_to_f32(to_np_bf16_bits(a)))     # the oracle's codes
+    codes, scales = torch.from_numpy(rc).cuda(), torch.from_numpy(rs).cuda()
+    announce("mxq_dequantize workload rows, strided output")
+    y = gpu.dequantize(codes, scales, wl.K)
+    full = torch.full((2048, wl.K + 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    gpu.dequantize(codes, scales, wl.K, out=full[:, :wl.K])
+    torch.cuda.synchronize()
+    ref_bits = oracle.f64_to_bf16_bits(oracle.dequantize_mxfp4(rc, rs, wl.K))
+    np.testing.assert_array_equal(to_np_bf16_bits(y), ref_bits)
+    np.testing.assert_array_equal(to_np_bf16_bits(full[:, :wl.K]), ref_bits)
+    assert bool((full[:, wl.K:] == 3.0).all())
