@@ -11,7 +11,8 @@ therefore the oracle's chain (quantize_mxfp4, gemm_w4a4) within the GEMM bar.
   every product normal and finite in one of the runs;
 * bit-identity with the unfused chain on tile-spanning shapes with ragged M / N tails,
   2 to 54 K-windows, row-strided activations and outputs, K off the fast path, binary32
-  activations, both rules, the Wan2.2 FFN-down workload at reduced and full size;
+  activations, both rules, the Wan2.2 FFN-down workload at reduced size and the Wan2.2
+  FFN-down and FLUX FFN-up / FFN-down workloads at full size;
 * the oracle chain within the bar on the tiny workload (binary32) and sampled outputs.
 """
 
@@ -183,12 +184,12 @@ def test_fused_workload_bitwise_and_oracle(gpu, name, M):
     assert ok.all()
 
 
-def test_fused_full_size_bitwise(gpu):
-    name = "wan_ffn_down_sqnr"
+@pytest.mark.parametrize("name", ["wan_ffn_down_sqnr", "flux_ffn_up_w4a4", "flux_ffn_down_w4a4"])
+def test_fused_full_size_bitwise(gpu, name):
     a, w = workloads.workload_inputs(name, device="cuda")
     wc, wsc = gpu.quantize(w)
     announce(f"fused full size {name} {tuple(a.shape)}")
     out = gpu.gemm_w4a4_fused(a, wc, wsc)
     ref = _chain(gpu, a, wc, wsc, "ocp")
     torch.cuda.synchronize()
-    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), "full-size fused output differs from the chain"
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{name}: full-size fused output differs from the chain"

@@ -131,7 +131,7 @@ def _sample_rows_cols(M, N, seed, nr=40, nc=48):
     return rows, cols
 
 
-@pytest.mark.parametrize("name", ["wan_ffn_down_sqnr", "flux_ffn_up_w4a4", "flux_qkv_w4a4"])
+@pytest.mark.parametrize("name", ["wan_ffn_down_sqnr", "flux_ffn_up_w4a4", "flux_ffn_down_w4a4", "flux_qkv_w4a4"])
 def test_w4a4_full_size_sampled(gpu, name):
     wl = workloads.WORKLOADS[name]
     a, w = workloads.workload_inputs(name, device="cuda")
