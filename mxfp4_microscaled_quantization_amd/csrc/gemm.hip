@@ -1826,8 +1826,8 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
     if (K > 0 && K % Fast<MD>::K_WIN == 0 && (scales_ok || !needs_scales)) {
       p.nwin = (int)(K / Fast<MD>::K_WIN);
       // the bf16 reference runs two waves per SIMD (measured faster); the scaled modes one
-      // (with the 64 x 128 wave tile their fragment reads per MFMA grow by half and the
-      // LDS becomes the limit)
+      // (measured slower with two: 64 x 128 wave tiles read half again as many fragments
+      // per MFMA)
       if constexpr (MD == GEMM_BF16)
         hipLaunchKernelGGL(gemm_fast8_kernel<MD>, grid, dim3(NT8), 0, stream, p);
       else
