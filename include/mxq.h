@@ -121,7 +121,6 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int6
                                  uint8_t* scales, int64_t ld_scales, void* stream);
 
 /*
- * mxq_quantize_fp8 --/*
  * mxq_quantize_fp8 -- static FP8 E4M3 activation quantization for W4A8 ([Q13]).
  *   q = E4M3(fl32(x * inv_scale)): one binary32 multiply (round to nearest even), then
  *   E4M3 round-to-nearest-even saturating at +-448 (never NaN); sign bit from the product.

@@ -47,15 +47,16 @@ constexpr int NT = 256;   // threads per workgroup
 constexpr int GROUP_M = 4;
 
 template <int MODE> struct Cfg;
-// NS: LDS stages of the fast path (a window's loads get NS-1 windows of compute to land)
+// Geometry of the generic (register-staged) kernel: bytes per row per window of the
+// activation / weight tiles, MFMA steps per window, K elements per window.
 template <> struct Cfg<GEMM_W4A4> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NS = 2;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256;
 };
 template <> struct Cfg<GEMM_W4A8> {
-  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NS = 3;
+  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128;
 };
 template <> struct Cfg<GEMM_BF16> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NS = 2;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64;
 };
 
 // Fast-path geometry.  A_RB / W_RB: bytes per row per K-window for the activation / weight
@@ -451,7 +452,6 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   using C = Fast<MODE>;
   constexpr uint32_t A_TILE = BM * C::A_RB;
   constexpr uint32_t W_TILE = BN * C::W_RB;
-  constexpr uint32_t BUF = A_TILE + W_TILE;    // one tile stage
   constexpr int A_LINES = A_TILE / 1024 / 4;   // 1 KB LDS lines per wave per window
   constexpr int W_LINES = W_TILE / 1024 / 4;
   constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
