@@ -226,8 +226,6 @@ def main():
         "device": torch.cuda.get_device_name(0),
     }
 
-    # ---- outside the timed step: the UOS scale rule (quantize rate, W4A4 SQNR on the same
-    # workload, both operands quantized with UOS) ----
     def time_fn(fn, n=10):
         fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -238,6 +236,27 @@ def main():
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    # ---- outside the timed step: the MFMA ceiling on the step's own operand bits. A
+    # register-only loop of each GEMM's MFMA instruction on fragments gathered from its
+    # operands (no memory traffic) gives what the matrix cores sustain on this data at the
+    # clock the chip holds under it; each GEMM's fraction of that ceiling beside it ----
+    waves = 4096
+    sink = torch.empty(waves * 64, dtype=torch.float32, device=dev)
+    ceiling = {"what": "register-only loop of the GEMM's MFMA instruction on fragments of the step's operands"}
+    for name, mode, ops, iters in (("mxq_gemm_w4a4", "w4a4", (ac, asc, wc, wsc), 1500),
+                                   ("mxq_gemm_w4a8", "w4a8", (a8, None, wc, wsc), 1000),
+                                   ("mxq_gemm_bf16", "bf16", (a, None, w, None), 1500)):
+        ms_c = time_fn(lambda: mxq.mfma_ceiling(mode, *ops, waves=waves, iters=iters, sink=sink), n=3)
+        rate_c = waves * iters * 16 * mxq.MFMA_FLOP[mode] / (ms_c * 1e-3) / 1e12
+        peak = work[name][2]
+        ceiling[name] = {"achieved": round(rate_c, 2), "unit": "TFLOP/s", "peak": peak,
+                         "frac_of_peak": round(rate_c / peak, 4),
+                         "gemm_frac_of_ceiling": round(kinfo[name]["achieved"] / rate_c, 4)}
+    res["mfma_ceiling"] = ceiling
+    del sink
+
+    # ---- the UOS scale rule (quantize rate, W4A4 SQNR on the same workload, both operands
+    # quantized with UOS) ----
     ms_uos = time_fn(lambda: mxq.quantize_into(a, ac, asc, rule="uos"))
     wc_u, wsc_u = mxq.quantize(w, rule="uos")
     mxq.quantize_into(a, ac, asc, rule="uos")

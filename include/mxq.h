@@ -220,6 +220,35 @@ mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t*
                           int64_t ld_scales, int64_t rows, int64_t cols, uint16_t* y,
                           int64_t ld_y, void* stream);
 
+/*
+ * Measurement aid (not part of the quantize / GEMM path).
+ *
+ * mxq_mfma_ceiling -- the MFMA throughput the chip sustains on the operand bits of a GEMM
+ * call, with no memory traffic.  The MI355X holds its power under these GEMMs by lowering
+ * its clock, and the energy of an MFMA grows with the operand bits that toggle, so this
+ * ceiling (not the dense peak) bounds what a GEMM can reach on the same data.
+ * Each lane of `waves` waves gathers 4 weight and 4 activation fragments (the bytes one
+ * lane of the GEMM's MFMA holds) from pseudo-random rows and 32-element blocks of the
+ * operand planes, with their scale bytes.  It then runs iters x 16 MFMAs of the GEMM's
+ * instruction on them in registers: v_mfma_scale_f32_32x32x64_f8f6f4 (W4A4, W4A8) or
+ * v_mfma_f32_32x32x16_bf16.  One wave per SIMD at a time.
+ * Work: waves * iters * 16 MFMAs of 2*32*32*64 FLOP (W4A4, W4A8) or 2*32*32*16 (bf16).
+ * mode   : which GEMM's operands: W4A4 a = activation codes, a_scales; W4A8 a = FP8 bytes
+ *          (a_scales unused); bf16 a = bf16 activations (no scales).  w / w_scales: the
+ *          weight codes and scales (W4A4, W4A8) or bf16 weights.  Layouts as for the GEMMs:
+ *          M x K activations and N x K weights, contiguous rows, bases 16-byte aligned.
+ * K      : a positive multiple of 32; M, N >= 1.
+ * waves  : a multiple of 4 in [4, 2^20]; iters in [1, 2^24].
+ * sink   : device float[waves * 64], owned by the caller: one value per lane (keeps the
+ *          work live; not a result).
+ * Errors : MXQ_ERR_UNSUPPORTED for an unknown mode, MXQ_ERR_INVALID_ARG for bad sizes or
+ *          pointers, checked before anything is enqueued.
+ */
+typedef enum { MXQ_GEMM_W4A4 = 0, MXQ_GEMM_W4A8 = 1, MXQ_GEMM_BF16 = 2 } mxq_gemm_mode;
+mxq_status mxq_mfma_ceiling(mxq_gemm_mode mode, const void* a, const uint8_t* a_scales,
+                            const void* w, const uint8_t* w_scales, int64_t M, int64_t N,
+                            int64_t K, int64_t waves, int64_t iters, float* sink, void* stream);
+
 /* Thread-local message for the last failing call on this thread ("" if none). Valid
  * until the next mxq_* call on the same thread. */
 const char* mxq_last_error(void);

@@ -20,6 +20,7 @@ import torch
 __all__ = [
     "lib", "MxqError", "quantize", "quantize_into", "quantize_hadamard", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
     "gemm_w4a4", "gemm_w4a4_fused", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_workspace_bytes", "dequantize",
+    "mfma_ceiling", "MFMA_FLOP",
     "LIB_PATH", "ABI_SYMBOLS",
 ]
 
@@ -47,6 +48,8 @@ ABI_SYMBOLS = {
     "mxq_sqnr_workspace_bytes": (_sz, [_i64]),
     "mxq_sqnr": (ctypes.c_int, [_ptr, _ptr, _i64, _i64, _i64, _i64, _ptr, _sz, _ptr, _ptr]),
     "mxq_dequantize": (ctypes.c_int, [_ptr, _i64, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
+    "mxq_mfma_ceiling": (ctypes.c_int, [ctypes.c_int, _ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _i64, _i64, _ptr,
+                                        _ptr]),
     "mxq_last_error": (ctypes.c_char_p, []),
     "mxq_abi_version": (ctypes.c_int, []),
 }
@@ -255,6 +258,40 @@ def gemm_bf16(a, w, out=None):
     out, ld = _out(M, N, a.device, out)
     _check(lib.mxq_gemm_bf16(_p(a), _p(w), M, N, K, _p(out), ld, _stream()))
     return out
+
+
+#: MFMA instruction FLOP per mode, as mxq_mfma_ceiling runs them
+MFMA_FLOP = {"w4a4": 2 * 32 * 32 * 64, "w4a8": 2 * 32 * 32 * 64, "bf16": 2 * 32 * 32 * 16}
+_GEMM_MODES = {"w4a4": 0, "w4a8": 1, "bf16": 2}
+
+
+def mfma_ceiling(mode: str, a, a_scales, w, w_scales, waves: int, iters: int, sink=None) -> int:
+    """Enqueue the register-only MFMA loop of mxq_mfma_ceiling on the operand planes of a
+    GEMM call (``mode`` "w4a4", "w4a8" or "bf16"; operands as for that GEMM, unused scales
+    None) on the current stream; returns the FLOP it performs."""
+    if mode not in _GEMM_MODES:
+        raise ValueError(f"mode must be one of {sorted(_GEMM_MODES)}")
+    if mode == "bf16":
+        _contig(a, "a", torch.bfloat16)
+        _contig(w, "w", torch.bfloat16)
+        M, K = a.shape
+    else:
+        _contig(a, "a", torch.uint8)
+        _contig(w, "w", torch.uint8)
+        _contig(w_scales, "w_scales", torch.uint8)
+        M = a.shape[0]
+        K = a.shape[1] * (2 if mode == "w4a4" else 1)
+        if mode == "w4a4":
+            _contig(a_scales, "a_scales", torch.uint8)
+    N = w.shape[0]
+    if sink is None:
+        sink = torch.empty(waves * 64, dtype=torch.float32, device=a.device)
+    elif sink.dtype != torch.float32 or sink.numel() < waves * 64 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 tensor of at least waves * 64 elements")
+    _check(lib.mxq_mfma_ceiling(_GEMM_MODES[mode], _p(a), _p(a_scales) if a_scales is not None else None, _p(w),
+                                _p(w_scales) if w_scales is not None else None, M, N, K, waves, iters, _p(sink),
+                                _stream()))
+    return waves * iters * 16 * MFMA_FLOP[mode]
 
 
 def sqnr_workspace_bytes(n: int) -> int:

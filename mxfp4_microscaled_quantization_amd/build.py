@@ -17,7 +17,7 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxq.so")
 ARCH = "gfx950"
 
-SOURCES = ["mxq_api.hip", "quantize.hip", "gemm.hip", "sqnr.hip"]
+SOURCES = ["mxq_api.hip", "quantize.hip", "gemm.hip", "sqnr.hip", "ceiling.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",

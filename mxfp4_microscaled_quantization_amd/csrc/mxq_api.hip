@@ -279,4 +279,30 @@ mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t*
                                                as_stream(stream)));
 }
 
+mxq_status mxq_mfma_ceiling(mxq_gemm_mode mode, const void* a, const uint8_t* a_scales, const void* w,
+                            const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, int64_t waves, int64_t iters,
+                            float* sink, void* stream) {
+  const char* fn = "mxq_mfma_ceiling";
+  if (mode != MXQ_GEMM_W4A4 && mode != MXQ_GEMM_W4A8 && mode != MXQ_GEMM_BF16)
+    return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown mode %d", fn, (int)mode);
+  if (M < 1 || N < 1 || K < 32 || K % 32 != 0)
+    return fail(MXQ_ERR_INVALID_ARG, "%s: need M, N >= 1 and K a positive multiple of 32 (M=%lld N=%lld K=%lld)", fn,
+                (long long)M, (long long)N, (long long)K);
+  if (M > (int64_t)0x7FFFFFFF || N > (int64_t)0x7FFFFFFF || K > ((int64_t)1 << 21))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: dimension too large", fn);
+  if (waves < 4 || waves % 4 != 0 || waves > ((int64_t)1 << 20))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: waves (%lld) must be a multiple of 4 in [4, 2^20]", fn, (long long)waves);
+  if (iters < 1 || iters > ((int64_t)1 << 24))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: iters (%lld) must be in [1, 2^24]", fn, (long long)iters);
+  mxq_status st;
+  if ((st = check_operand(fn, "a", a, M, K, 16)) != MXQ_OK) return st;
+  if ((st = check_operand(fn, "w", w, N, K, 16)) != MXQ_OK) return st;
+  if (mode != MXQ_GEMM_BF16 && !w_scales) return fail(MXQ_ERR_INVALID_ARG, "%s: w_scales is NULL", fn);
+  if (mode == MXQ_GEMM_W4A4 && !a_scales) return fail(MXQ_ERR_INVALID_ARG, "%s: a_scales is NULL", fn);
+  if (!sink || !aligned(sink, 4)) return fail(MXQ_ERR_INVALID_ARG, "%s: sink must be a non-NULL 4-byte aligned pointer", fn);
+  const mxq::GemmMode gm = mode == MXQ_GEMM_W4A4 ? mxq::GEMM_W4A4 : (mode == MXQ_GEMM_W4A8 ? mxq::GEMM_W4A8 : mxq::GEMM_BF16);
+  return hip_status(fn, mxq::launch_mfma_ceiling(gm, a, a_scales, w, w_scales, M, N, K, waves, iters, sink,
+                                                 as_stream(stream)));
+}
+
 }  // extern "C"

@@ -33,6 +33,12 @@ hipError_t launch_gemm_w4a4_fused(const void* a, bool f32, int64_t ld_a, const u
                                   int64_t M, int64_t N, int64_t K, bool uos, uint16_t* out, int64_t ld_out,
                                   hipStream_t stream);
 
+// Register-only MFMA loop on fragments gathered from a GEMM call's operand planes
+// (waves a multiple of 4; sink: one float per lane).
+hipError_t launch_mfma_ceiling(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,
+                               const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, int64_t waves, int64_t iters,
+                               float* sink, hipStream_t stream);
+
 size_t sqnr_workspace_bytes(int64_t n);
 hipError_t launch_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols,
                        int64_t ld_ref, int64_t ld_test, void* ws, double* out3, hipStream_t stream);

@@ -83,6 +83,14 @@ def _err():
     (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, None, FAKE, 8, 8, 64, 0, FAKE, 8, None), "w_codes is NULL"),
     (lambda L: L.mxq_gemm_w4a4_fused(None, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "NULL"),
     (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 4, None), "ld_out"),
+    (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 8, 8, 48, 4, 1, FAKE, None), "multiple of 32"),
+    (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 0, 8, 64, 4, 1, FAKE, None), "M, N >= 1"),
+    (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, 6, 1, FAKE, None), "waves"),
+    (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, 4, 0, FAKE, None), "iters"),
+    (lambda L: L.mxq_mfma_ceiling(0, FAKE, None, FAKE, FAKE, 8, 8, 64, 4, 1, FAKE, None), "a_scales is NULL"),
+    (lambda L: L.mxq_mfma_ceiling(1, FAKE, None, FAKE, None, 8, 8, 64, 4, 1, FAKE, None), "w_scales is NULL"),
+    (lambda L: L.mxq_mfma_ceiling(2, FAKE_ODD, None, FAKE, None, 8, 8, 64, 4, 1, FAKE, None), "aligned"),
+    (lambda L: L.mxq_mfma_ceiling(2, FAKE, None, FAKE, None, 8, 8, 64, 4, 1, None, None), "sink"),
 ])
 def test_invalid_arguments_are_rejected_before_launch(call, needle):
     st = call(mxq.lib)
@@ -101,6 +109,7 @@ def test_unknown_dtype_is_unsupported():
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 3, FAKE, 32, FAKE, 2, None), "scale rule"),
     (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 2, FAKE, 8, None), "scale rule"),
     (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 9, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "dtype"),
+    (lambda L: L.mxq_mfma_ceiling(3, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, 4, 1, FAKE, None), "mode"),
 ])
 def test_unknown_rule_or_block_is_unsupported(call, needle):
     st = call(mxq.lib)
