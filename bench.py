@@ -117,8 +117,8 @@ def cpu_baseline(name, rows, a_host_rows, w_bits):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}); "
-              "sharding across GPUs is described in DESIGN.md but not built.", file=sys.stderr)
+        print(f"bench.py: runs on one GPU only (asked for --gpus {args.gpus}); "
+              "the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
