@@ -245,7 +245,7 @@ def main():
     ceiling = {"what": "register-only loop of the GEMM's MFMA instruction on fragments of the step's operands"}
     for name, mode, ops, iters in (("mxq_gemm_w4a4", "w4a4", (ac, asc, wc, wsc), 1500),
                                    ("mxq_gemm_w4a8", "w4a8", (a8, None, wc, wsc), 1000),
-                                   ("mxq_gemm_bf16", "bf16", (a, None, w, None), 1500)):
+                                   ("mxq_gemm_bf16", "bf16", (a, None, w, None), 3000)):
         ms_c = time_fn(lambda: mxq.mfma_ceiling(mode, *ops, waves=waves, iters=iters, sink=sink), n=3)
         rate_c = waves * iters * 16 * mxq.MFMA_FLOP[mode] / (ms_c * 1e-3) / 1e12
         peak = work[name][2]

@@ -231,8 +231,8 @@ mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t*
  * lane of the GEMM's MFMA holds) from pseudo-random rows and 32-element blocks of the
  * operand planes, with their scale bytes.  It then runs iters x 16 MFMAs of the GEMM's
  * instruction on them in registers: v_mfma_scale_f32_32x32x64_f8f6f4 (W4A4, W4A8) or
- * v_mfma_f32_32x32x16_bf16.  One wave per SIMD at a time.
- * Work: waves * iters * 16 MFMAs of 2*32*32*64 FLOP (W4A4, W4A8) or 2*32*32*16 (bf16).
+ * v_mfma_f32_16x16x32_bf16.
+ * Work: waves * iters * 16 MFMAs of 2*32*32*64 FLOP (W4A4, W4A8) or 2*16*16*32 (bf16).
  * mode   : which GEMM's operands: W4A4 a = activation codes, a_scales; W4A8 a = FP8 bytes
  *          (a_scales unused); bf16 a = bf16 activations (no scales).  w / w_scales: the
  *          weight codes and scales (W4A4, W4A8) or bf16 weights.  Layouts as for the GEMMs:

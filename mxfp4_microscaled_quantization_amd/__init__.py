@@ -261,7 +261,7 @@ def gemm_bf16(a, w, out=None):
 
 
 #: MFMA instruction FLOP per mode, as mxq_mfma_ceiling runs them
-MFMA_FLOP = {"w4a4": 2 * 32 * 32 * 64, "w4a8": 2 * 32 * 32 * 64, "bf16": 2 * 32 * 32 * 16}
+MFMA_FLOP = {"w4a4": 2 * 32 * 32 * 64, "w4a8": 2 * 32 * 32 * 64, "bf16": 2 * 16 * 16 * 32}
 _GEMM_MODES = {"w4a4": 0, "w4a8": 1, "bf16": 2}
 
 

@@ -7,10 +7,13 @@
 // measures what the matrix cores sustain on the bits of a given call: every lane gathers
 // the bytes one lane of the GEMM's MFMA holds -- 4 weight and 4 activation fragments
 // from pseudo-random rows and 32-element blocks of the operand planes, with their scale
-// bytes -- and runs the GEMM's instruction on them in registers, cycling through the
-// 4 x 4 fragment pairs as a 128 x 128 wave tile does.  The fragments stay fixed across
+// bytes -- and runs the GEMM's instruction on them in registers (32 x 32 x 64 scaled MFMAs
+// for W4A4 / W4A8, 16 x 16 x 32 for bf16), cycling through the 4 x 4 fragment pairs as
+// a wave tile does.  The fragments stay fixed across
 // iterations, so operands toggle a little less than in the GEMM: the ceiling is, if
 // anything, optimistic.
+#include <type_traits>
+
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -54,8 +57,10 @@ __device__ __forceinline__ v8i gather(const uint8_t* base, int64_t rows, int64_t
   return v;
 }
 
+// One wave per SIMD for the scaled modes (256 accumulator registers, as in their GEMM);
+// two for bf16, as in its GEMM, which keeps the accumulators in VGPRs
 template <int MODE>
-__global__ __launch_bounds__(256, 1) void mfma_ceiling_kernel(CeilingParams p) {
+__global__ __launch_bounds__(256, MODE == GEMM_BF16 ? 2 : 1) void mfma_ceiling_kernel(CeilingParams p) {
   const uint32_t gid = blockIdx.x * 256u + threadIdx.x;
   // bytes per lane fragment and per row of each operand plane
   constexpr int WB = 16;                                        // fp4: 32 elements; bf16: 8
@@ -73,13 +78,16 @@ __global__ __launch_bounds__(256, 1) void mfma_ceiling_kernel(CeilingParams p) {
     fa[i] = gather<AB>(p.a, p.M, a_rb, mix32(gid * 16u + 8u + (uint32_t)i), r, c);
     sca[i] = MODE == GEMM_W4A4 ? (int)p.a_scales[r * sc_rb + c] : 127;
   }
-  v16f acc[4][4];
+  // the scaled modes' GEMM runs 32 x 32 x 64 MFMAs, the bf16 reference 16 x 16 x 32
+  using Acc = typename std::conditional<MODE == GEMM_BF16, v4f, v16f>::type;
+  constexpr int AE = MODE == GEMM_BF16 ? 4 : 16;
+  Acc acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < AE; ++e) acc[i][j][e] = 0.0f;
   for (int it = 0; it < p.iters; ++it) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(256, 1) void mfma_ceiling_kernel(CeilingParams p) {
         else if constexpr (MODE == GEMM_W4A8)
           acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fw[i], fa[j], acc[i][j], 4, 0, 0, scw[i], 0, 127);
         else
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
               __builtin_bit_cast(bf16x8, __builtin_shufflevector(fw[i], fw[i], 0, 1, 2, 3)),
               __builtin_bit_cast(bf16x8, __builtin_shufflevector(fa[j], fa[j], 0, 1, 2, 3)), acc[i][j], 0, 0, 0);
       }
@@ -102,7 +110,7 @@ __global__ __launch_bounds__(256, 1) void mfma_ceiling_kernel(CeilingParams p) {
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) s += acc[i][j][e];
+      for (int e = 0; e < AE; ++e) s += acc[i][j][e];
   p.sink[gid] = s;
 }
 

@@ -28,11 +28,13 @@
 //  * Workgroups are renumbered so that each XCD (dispatched round-robin) walks a
 //    contiguous run of tiles, grouped 4 m-tiles wide, keeping panels shared in its L2.
 //  * Ragged M/N/K tails are zero-filled by buffer-load range checks and masked stores.
-//  * The bf16 reference runs an eight-wave variant (two waves per SIMD, 64 x 128 per
-//    wave), which issues its memory and LDS instructions alongside the other wave's MFMAs.
+//  * The bf16 reference (gemm_bf16_kernel) uses 16 x 16 x 32 MFMAs in eight waves (two per
+//    SIMD, 128 x 64 per wave): under the chip's power limit that shape sustains more
+//    MFMA throughput on real data than 32 x 32 x 16.
 //  * gemm_w4a4_fused8_kernel takes unquantized activations and quantizes each activation
 //    tile into LDS inside the GEMM, bit-identically to the separate quantizer.
 #include <type_traits>
+#include <utility>
 
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
@@ -59,21 +61,22 @@ template <> struct Cfg<GEMM_BF16> {
   static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64;
 };
 
-// Fast-path geometry.  A_RB / W_RB: bytes per row per K-window for the activation / weight
-// tile (128 bytes: whole cache lines per row); STEPS: 32x32 MFMA steps per window; NA / NW:
-// depth of the activation / weight tile rings in LDS (a window's loads get about NA-1
-// windows of compute to land); SC_WIN: scale bytes per row
-// per window.  Lane group g at step t holds K-chunk g * STEPS + t of the weight row (and of
-// the activation row for FP4 / bf16 activations).
+// Fast-path geometry of gemm_fast_kernel (the scaled modes).  A_RB / W_RB: bytes per row
+// per K-window for the activation / weight tile (128 bytes: whole cache lines per row);
+// STEPS: 32x32 MFMA steps per window; NS: depth of both tile rings in LDS (a window's
+// loads get about NS-1 windows of compute to land); SC_WIN: scale bytes per row per
+// window.  Lane group g at step t holds K-chunk g * STEPS + t of the weight row (and of
+// the activation row for FP4 activations).  The bf16 reference has its own kernel
+// (gemm_bf16_kernel) over windows of K_WIN elements.
 template <int MODE> struct Fast;
 template <> struct Fast<GEMM_W4A4> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NA = 2, NW = 2, SC_WIN = 8;
+  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 256, NS = 2, SC_WIN = 8;
 };
 template <> struct Fast<GEMM_W4A8> {
-  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NA = 3, NW = 3, SC_WIN = 4;
+  static constexpr int A_RB = 128, W_RB = 64, STEPS = 2, K_WIN = 128, NS = 3, SC_WIN = 4;
 };
 template <> struct Fast<GEMM_BF16> {
-  static constexpr int A_RB = 128, W_RB = 128, STEPS = 4, K_WIN = 64, NA = 3, NW = 2, SC_WIN = 0;
+  static constexpr int K_WIN = 64;
 };
 
 // s_waitcnt immediate (gfx9 encoding): vmcnt <= vm, lgkmcnt <= 0, expcnt unconstrained
@@ -383,8 +386,8 @@ __device__ __forceinline__ void load_line_to_lds(__amdgpu_buffer_rsrc_t r, uint8
 }
 
 // Fragments of MFMA step t from one LDS stage.  Lane group g (lanes 32g..32g+31) at step t
-// holds K-chunk g * STEPS + t of its weight row (fp4: one 32-element block; bf16: 8
-// elements) and the same chunk of its activation row; FP8 activation rows give each lane
+// holds K-chunk g * STEPS + t of its weight row (one 32-element FP4 block) and the same
+// chunk of its FP4 activation row; FP8 activation rows give each lane
 // the chunks 2t+g and 4+2t+g that the FP8 operand layout pairs with those FP4 blocks.
 //
 // `after(k)` runs after the k-th read (k = 0 .. 7, or 11 for W4A8).  LDS-DMA loads issued
@@ -431,6 +434,7 @@ constexpr int dma_after(int k, int n, int rd) { return (k + 1) * n / rd - k * n 
 template <int MODE, int T>
 __device__ __forceinline__ void mfma16(v16f (&acc)[4][4], const v4i (&f)[12], const uint32_t (&scw)[4],
                                        const uint32_t (&sca)[4]) {
+  static_assert(MODE == GEMM_W4A4 || MODE == GEMM_W4A8, "scaled modes only");
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -438,12 +442,9 @@ __device__ __forceinline__ void mfma16(v16f (&acc)[4][4], const v4i (&f)[12], co
       if constexpr (MODE == GEMM_W4A4)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), widen(f[4 + j]), acc[i][j], 4, 4, T,
                                                                     (int)scw[i], T, (int)sca[j]);
-      else if constexpr (MODE == GEMM_W4A8)
+      else
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), cat(f[4 + j], f[8 + j]), acc[i][j],
                                                                     4, 0, T, (int)scw[i], 0, 127);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                            __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
     }
 }
 
@@ -456,17 +457,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   constexpr int W_LINES = W_TILE / 1024 / 4;
   constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
   constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
-  constexpr int NA = C::NA, NW = C::NW;
-  // Equal rings: window w+N's activation tile goes out at the hand-over of window w into
-  // the slot it releases, its weight tile under the next window's step 0.  Deeper
-  // activation ring (the bf16 reference, whose activations stream from HBM while the
-  // weights stay in the last-level caches): the weight tile of window w+NW goes out at the
-  // hand-over, the activation tile of window w+NA-1 under step 0 of window w, so
-  // activations get about two windows to land and weights one.
-  constexpr bool SPLIT = NA != NW;
-  static_assert(!SPLIT || (NA == 3 && NW == 2), "split rings: three activation, two weight slots");
-  constexpr int NS = NA;                       // windows issued ahead by the prologue + 1
-  constexpr uint32_t W_BASE = NA * A_TILE, SC_BASE = NA * A_TILE + NW * W_TILE;
+  static_assert(MODE != GEMM_BF16, "the bf16 reference runs gemm_bf16_kernel");
+  // Window w+NS's activation tile goes out at the hand-over of window w into the slot it
+  // releases, its weight tile under the next window's step 0.
+  constexpr int NS = C::NS;                    // windows issued ahead by the prologue + 1
+  constexpr uint32_t W_BASE = NS * A_TILE, SC_BASE = NS * A_TILE + NS * W_TILE;
   // Scales travel in chunks of SC_ROW bytes per row (CW windows) through a two-slot ring
   // beside the tile stages: a load instruction costs the memory pipeline per cache line
   // touched, so a few bytes per row per window would cost as much as the tiles themselves.
@@ -530,8 +525,8 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // four waves never queue a whole window of DMA at once: part 0 = activation tile,
   // part 1 = weight tile.
   // ring slots of window w's tiles
-  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NA) * A_TILE; };
-  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NW) * W_TILE; };
+  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NS) * A_TILE; };
+  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NS) * W_TILE; };
   // one line of window w's tile: part 0 = activation tile, part 1 = weight tile
   auto issue_line = [&](int w, auto part_tag, int j) {
     constexpr int PART = decltype(part_tag)::value;
@@ -601,10 +596,10 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   v4i f0[12], f1[12];
   constexpr int RD = (MODE == GEMM_W4A8) ? 12 : 8;       // ds_read_b128 per fragment set
   constexpr int VM = A_LINES + W_LINES;                  // tile DMA loads per wave per window
-  // tile loads issued under step 0 (VM1) and at the hand-over (VM0)
-  constexpr int VM1 = SPLIT ? A_LINES : W_LINES, VM0 = SPLIT ? W_LINES : A_LINES;
+  // tile loads issued under step 0 (VM1: weight tile) and at the hand-over (VM0: activation tile)
+  constexpr int VM1 = W_LINES, VM0 = A_LINES;
   // loads allowed in flight when the hand-over has to see window w+1 complete
-  constexpr int WAIT_VM = SPLIT ? A_LINES : (NA - 2) * VM;
+  constexpr int WAIT_VM = (NS - 2) * VM;
 
   // prologue: window 0 and scale chunk 0 resident, chunk 1 and windows 1 .. NS-1 in flight
   // (the chunk first, so the hand-over wait counts below see only tile loads after it),
@@ -616,17 +611,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   if constexpr (HAS_SC)
     if (nchunks > 1) issue_chunk(1);
 #pragma unroll
-  for (int k = 1; k < (SPLIT ? 2 : NS); ++k)
+  for (int k = 1; k < NS; ++k)
     if (k < nwin) issue_loads(k);
   read_frags<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
   read_scales(0, scw, sca);
 
-  // One window.  PEND: the step-0 tile loads go out (equal rings: the weight tile of window
-  // w+NS-1, whose activation tile went out at the previous hand-over; split rings: the
-  // activation tile of window w+NA-1).  STEADY: the hand-over waits for window w+1 only
-  // and refills the slot(s) this window releases (equal rings: activation tile of window
-  // w+NS; split rings: weight tile of window w+NW).  The tail waits for everything and
-  // loads no tiles.  Memory-free MFMAs cannot be sunk past the barrier: every step is its
+  // One window.  PEND: the step-0 tile loads go out (the weight tile of window w+NS-1,
+  // whose activation tile went out at the previous hand-over).  STEADY: the hand-over
+  // waits for window w+1 only and refills the slot this window releases with the
+  // activation tile of window w+NS.  The tail waits for everything and loads no tiles.  Memory-free MFMAs cannot be sunk past the barrier: every step is its
   // own scheduling region.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
@@ -641,12 +634,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     // step-0 tile loads, spread over the reads of step 0
     auto pend_loads = [&](int k) {
       if constexpr (PEND) {
-        if (dma_after(k, VM1, RD) > 0) {
-          if constexpr (SPLIT)
-            issue_line(w + NA - 1, I0{}, k * VM1 / RD);
-          else
-            issue_line(w + NS - 1, I1{}, k * VM1 / RD);
-        }
+        if (dma_after(k, VM1, RD) > 0) issue_line(w + NS - 1, I1{}, k * VM1 / RD);
       }
     };
     // Steps 0 .. STEPS-2, one scheduling region each (a region boundary after every step
@@ -707,12 +695,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     // refill the slot just released, spread over the next window's step-0 reads
     read_frags<MODE>(f0, a_slot(w + 1), w_slot(w + 1), wm, wn, lane, 0, [&](int k) {
       if constexpr (STEADY) {
-        if (dma_after(k, VM0, RD) > 0) {
-          if constexpr (SPLIT)
-            issue_line(w + NW, I1{}, k * VM0 / RD);
-          else
-            issue_line(w + NS, I0{}, k * VM0 / RD);
-        }
+        if (dma_after(k, VM0, RD) > 0) issue_line(w + NS, I0{}, k * VM0 / RD);
       }
     });
     if constexpr (C::STEPS == 4)
@@ -736,10 +719,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   using T_ = std::true_type;
   using F_ = std::false_type;
   int w = 0;
-  if constexpr (SPLIT) {
-    // windows 0 and 1 come from the prologue; window w loads tiles of window w+2
-    for (; w < nwin - 2; ++w) window(w, T_{}, T_{});
-  } else if (nwin > NS) {
+  if (nwin > NS) {
     window(0, F_{}, T_{});
     for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{});
     window(w, T_{}, F_{});
@@ -1073,366 +1053,224 @@ __global__ __launch_bounds__(NT, 1) void gemm_w4a4_fused_generic_kernel(Params p
 }
 
 // ---------------------------------------------------------------------------------
-// Eight-wave fast path: the same pipeline as gemm_fast_kernel with two waves per SIMD.
-// A wave issues at most one instruction per few cycles whatever its type, and a second
-// wave on the SIMD issues in parallel, so the DMA, scale and LDS-read instructions of one
-// wave no longer hold back the matrix core while the other wave's MFMAs run.  Each wave
-// owns a 64 (m) x 128 (n) sub-tile: 4 weight fragments x 2 activation fragments, 8
-// accumulators (128 AGPRs), 8 MFMAs per step.  Every 32 x 32 output block still gets the
-// same MFMAs in the same order as in the four-wave kernel.
-constexpr int NT8 = 512;
+// bf16 reference GEMM: 16 x 16 x 32 MFMAs, eight waves (two per SIMD).
+//
+// Under these GEMMs the chip runs below its top clock to stay within its power, and the
+// energy of an MFMA grows with the operand bits that toggle.  With real bf16 operands a
+// register-only loop of v_mfma_f32_16x16x32_bf16 sustains ~14 % more than one of
+// v_mfma_f32_32x32x16_bf16, at the same work per element.  The 16 x 16 shape needs two
+// waves per SIMD to keep the matrix core fed.  Each wave owns 128 (m) x 64 (n): 8
+// activation and 4 weight fragments of 16 rows, 32 accumulators of 4 registers, 32 MFMAs
+// per step, two steps (K = 32 each) per 64-element window.
+//
+// Lane layout of the 16 x 16 MFMA (pinned on the GPU): lane l holds row l & 15 of a
+// fragment and K-group g = l >> 4 (8 bf16 each); both operands use the same layout, so
+// any assignment of K to lane groups that they share is valid.  Lane group g at step t
+// reads the 16-byte chunk g + 4t of its rows: with the 128-byte-row swizzle, the four
+// lane groups of a ds_read_b128 then touch distinct banks (chunk 2g + t conflicts).  The
+// output of block (i, j) sits in lane l as columns 4g .. 4g+3 of row l & 15.
+//
+// Pipeline (same DMA, swizzle and epilogue staging as gemm_fast_kernel): three activation
+// slots and two weight slots of 32 KB.  The hand-over of window w releases both of its
+// slots; the weight tile of window w+2, then the activation tile of window w+3, go out
+// under the next step's MFMAs, so activation tiles (streamed from HBM) get about two
+// windows to land and weight tiles one.  Tile order: groups one m-tile wide
+// (tile_origin).  Measured on the Wan2.2 FFN-down shape against the 32 x 32 eight-wave
+// kernel it replaces: 7.40-7.64 ms vs 7.53-7.83 ms.
+constexpr int NT16 = 512;
 
-// Fragments of MFMA step t for the eight-wave layout: weight rows wn*128 + 32i (i < 4)
-// into f[0..3], activation rows wm*64 + 32j (j < 2) into f[4..5] (FP8: low halves
-// f[4..5], high halves f[6..7]).  `after(k)` runs after the k-th read.
-template <int MODE, class After>
-__device__ __forceinline__ void read_frags8(v4i (&f)[8], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
-                                            uint32_t lane, int t, After&& after) {
-  using F = Fast<MODE>;
-  const uint32_t g = lane >> 5, r32 = lane & 31;
-  const uint32_t chunk = g * F::STEPS + t;
+// Step-t fragments of one LDS stage: f[0..3] weight rows wn*64 + 16i + (l & 15),
+// f[4..11] activation rows wm*128 + 16j + (l & 15); after(k) runs after the k-th read.
+template <class After>
+__device__ __forceinline__ void read_frags_bf16(v4i (&f)[12], const uint8_t* la, const uint8_t* lw, uint32_t wm,
+                                                uint32_t wn, uint32_t lane, int t, After&& after) {
+  const uint32_t r16 = lane & 15, chunk = (lane >> 4) + 4 * t;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    f[i] = *reinterpret_cast<const v4i*>(lw + swz<F::W_RB>(wn * 128 + 32 * i + r32, chunk));
+    f[i] = *reinterpret_cast<const v4i*>(lw + swz128(wn * 64 + 16 * i + r16, chunk));
     after(i);
   }
-  if constexpr (MODE == GEMM_W4A8) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t row = wm * 64 + 32 * j + r32;
-      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 2 * t + g));
-      after(4 + 2 * j);
-      f[6 + j] = *reinterpret_cast<const v4i*>(la + swz128(row, 4 + 2 * t + g));
-      after(5 + 2 * j);
-    }
-  } else {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      f[4 + j] = *reinterpret_cast<const v4i*>(la + swz<F::A_RB>(wm * 64 + 32 * j + r32, chunk));
-      after(4 + j);
-    }
+  for (int j = 0; j < 8; ++j) {
+    f[4 + j] = *reinterpret_cast<const v4i*>(la + swz128(wm * 128 + 16 * j + r16, chunk));
+    after(4 + j);
   }
 }
 
-template <int MODE>
-__device__ __forceinline__ void read_frags8(v4i (&f)[8], const uint8_t* la, const uint8_t* lw, uint32_t wm, uint32_t wn,
-                                            uint32_t lane, int t) {
-  read_frags8<MODE>(f, la, lw, wm, wn, lane, t, [](int) {});
-}
-
-template <int MODE, int T>
-__device__ __forceinline__ void mfma8(v16f (&acc)[4][2], const v4i (&f)[8], const uint32_t (&scw)[4],
-                                      const uint32_t (&sca)[2]) {
+__device__ __forceinline__ void mfma_bf16_step(v4f (&acc)[4][8], const v4i (&f)[12]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if constexpr (MODE == GEMM_W4A4)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), widen(f[4 + j]), acc[i][j], 4, 4, T,
-                                                                    (int)scw[i], T, (int)sca[j]);
-      else if constexpr (MODE == GEMM_W4A8)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(f[i]), cat(f[4 + j], f[6 + j]), acc[i][j],
-                                                                    4, 0, T, (int)scw[i], 0, 127);
-      else
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, f[i]),
-                                                            __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
-    }
+    for (int j = 0; j < 8; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, f[i]),
+                                                          __builtin_bit_cast(bf16x8, f[4 + j]), acc[i][j], 0, 0, 0);
 }
 
-// One scheduling region of the eight-wave kernel: `reads` LDS reads, `vm` DMA loads spread
-// over them (dma_after), 8 MFMAs.
-template <int READS, int VM>
-__device__ __forceinline__ void interleave8() {
-  constexpr int N = READS > 8 ? READS : 8;
-#pragma unroll
-  for (int r = 0; r < N; ++r) {
-    if (r < READS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-    if (r < READS && VM > 0 && dma_after(r, VM, READS) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    if (r < 8) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-  }
+// Scheduling pattern of one MFMA region: unit I is one fragment read, then (DMA) one tile
+// load when the VMN loads spread over the RDN reads fall there, then its share of the
+// region's MFMAS MFMAs.
+template <int ID, int R, int MFMAS, int VMN, bool DMA, int I>
+__device__ __forceinline__ void sched_unit() {
+  __builtin_amdgcn_sched_group_barrier(0x100, 1, ID);
+  if constexpr (DMA && dma_after(I, VMN, R) > 0) __builtin_amdgcn_sched_group_barrier(0x020, 1, ID);
+  constexpr int n = (I + 1) * MFMAS / R - I * MFMAS / R;
+  if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x008, n, ID);
+}
+template <int ID, int R, int MFMAS, int VMN, bool DMA, int... Is>
+__device__ __forceinline__ void sched_units(std::integer_sequence<int, Is...>) {
+  (sched_unit<ID, R, MFMAS, VMN, DMA, Is>(), ...);
 }
 
-template <int MODE>
-__global__ __launch_bounds__(NT8, 1) void gemm_fast8_kernel(Params p) {
-  using C = Fast<MODE>;
-  constexpr int WAVES = NT8 / 64;
-  constexpr uint32_t A_TILE = BM * C::A_RB;
-  constexpr uint32_t W_TILE = BN * C::W_RB;
-  constexpr int A_LINES = A_TILE / 1024 / WAVES;   // 1 KB LDS lines per wave per window
-  constexpr int W_LINES = W_TILE / 1024 / WAVES;
-  constexpr int A_ROWS_PER_LINE = 1024 / C::A_RB;
-  constexpr int W_ROWS_PER_LINE = 1024 / C::W_RB;
-  constexpr int NA = C::NA, NW = C::NW;
-  constexpr bool SPLIT = NA != NW;
-  static_assert(!SPLIT || (NA == 3 && NW == 2), "split rings: three activation, two weight slots");
-  constexpr int NS = NA;
-  constexpr uint32_t W_BASE = NA * A_TILE, SC_BASE = NA * A_TILE + NW * W_TILE;
-  constexpr uint32_t SC_WIN = C::SC_WIN;
-  constexpr bool HAS_SC = SC_WIN > 0;
-  constexpr uint32_t SC_ROW = 32;
-  constexpr int CW = HAS_SC ? (int)(SC_ROW / SC_WIN) : 1;
-  constexpr uint32_t SC_ROWS = HAS_SC ? BN + (MODE == GEMM_W4A4 ? BM : 0) : 0;
-  constexpr uint32_t SLOT = SC_ROWS * SC_ROW;
-  constexpr int SC_LINES = (int)(SLOT / 1024 / WAVES);
-  static_assert(!HAS_SC || SC_LINES >= 1, "a scale chunk line per wave");
-  constexpr uint32_t LDS_BYTES = SC_BASE + 2 * SLOT > 8u * 16384u ? SC_BASE + 2 * SLOT : 8u * 16384u;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[LDS_BYTES];
+__global__ __launch_bounds__(NT16, 1) void gemm_bf16_kernel(Params p) {
+  constexpr int WAVES = NT16 / 64;
+  constexpr int NA = 3, NW = 2;                       // activation / weight ring slots
+  constexpr uint32_t RB = 128;                        // bytes per row per window (64 bf16)
+  constexpr uint32_t TILE = BM * RB;                  // 32 KB (BM == BN)
+  constexpr int LINES = (int)(TILE / 1024 / WAVES);   // 4 DMA lines per wave per tile
+  constexpr int ROWS_PER_LINE = 1024 / RB;
+  constexpr uint32_t W_BASE = NA * TILE;
+  static_assert(BM == BN && 4 * 128 * 256 <= (NA + NW) * TILE, "output staging fits the rings");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[(NA + NW) * TILE];
 
   const uint32_t tid = threadIdx.x, lane = tid & 63;
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
-  const uint32_t wm = wave & 3, wn = wave >> 2;
-
+  const uint32_t wm = wave & 1, wn = wave >> 1;
   int m0, n0;
   tile_origin(p, m0, n0);
   const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
-  const bool has_ws = MODE != GEMM_BF16, has_as = MODE == GEMM_W4A4;
-  const __amdgpu_buffer_rsrc_t rsw =
-      make_rsrc(has_ws ? p.w_scales + (int64_t)n0 * p.scale_row_bytes : p.w, has_ws ? rows_w * p.scale_row_bytes : 0);
-  const __amdgpu_buffer_rsrc_t rsa =
-      make_rsrc(has_as ? p.a_scales + (int64_t)m0 * p.scale_row_bytes : p.a, has_as ? rows_a * p.scale_row_bytes : 0);
 
-  constexpr uint32_t A_CPR = C::A_RB / 16, W_CPR = C::W_RB / 16;
-  auto dma_voffs = [&](uint32_t cpr, uint32_t row_bytes, uint32_t& even, uint32_t& odd) {
-    const uint32_t row = lane / cpr, slot = lane % cpr;
-    if (cpr == 8) {
-      even = row * row_bytes + ((slot ^ ((row >> 1) & 7u)) * 16);
-      odd = row * row_bytes + ((slot ^ (((8u + row) >> 1) & 7u)) * 16);
-    } else {
-      even = odd = row * row_bytes + ((slot ^ ((row >> 2) & 3u)) * 16);
-    }
+  // direct-to-LDS lines: LDS line q holds rows 8q .. 8q+7; lane i lands at byte 16 i, in
+  // row i / 8 at slot i % 8, and fetches the chunk the swizzle maps there (the swizzle
+  // term (r >> 1) & 7 depends on the line's parity)
+  const uint32_t drow = lane >> 3, dslot = lane & 7;
+  const uint32_t swz_even = (dslot ^ ((drow >> 1) & 7u)) * 16, swz_odd = (dslot ^ (((8u + drow) >> 1) & 7u)) * 16;
+  const uint32_t a_voff0 = drow * p.a_row_bytes + swz_even, a_voff1 = drow * p.a_row_bytes + swz_odd;
+  const uint32_t w_voff0 = drow * p.w_row_bytes + swz_even, w_voff1 = drow * p.w_row_bytes + swz_odd;
+  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NA) * TILE; };
+  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NW) * TILE; };
+  auto issue_a = [&](int w, int j) {
+    const uint32_t line = wave * LINES + j;
+    load_line_to_lds(ra, a_slot(w) + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+                     (uint32_t)w * RB + line * ROWS_PER_LINE * p.a_row_bytes);
   };
-  uint32_t a_voff0, a_voff1, w_voff0, w_voff1;
-  dma_voffs(A_CPR, p.a_row_bytes, a_voff0, a_voff1);
-  dma_voffs(W_CPR, p.w_row_bytes, w_voff0, w_voff1);
-  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
-
-  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NA) * A_TILE; };
-  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NW) * W_TILE; };
-  auto issue_line = [&](int w, auto part_tag, int j) {
-    constexpr int PART = decltype(part_tag)::value;
-    if constexpr (PART == 0) {
-      const uint32_t line = wave * A_LINES + j;
-      load_line_to_lds(ra, a_slot(w) + line * 1024, (line & 1) ? a_voff1 : a_voff0,
-                       (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
-    } else {
-      const uint32_t line = wave * W_LINES + j;
-      load_line_to_lds(rw, w_slot(w) + line * 1024, (line & 1) ? w_voff1 : w_voff0,
-                       (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
-    }
-  };
-  auto issue_loads = [&](int w) {
-#pragma unroll
-    for (int j = 0; j < A_LINES; ++j) issue_line(w, std::integral_constant<int, 0>{}, j);
-#pragma unroll
-    for (int j = 0; j < W_LINES; ++j) issue_line(w, std::integral_constant<int, 1>{}, j);
-  };
-  const int nchunks = (p.nwin + CW - 1) / CW;
-  auto issue_chunk = [&](int c) {
-    uint8_t* slot = lds + SC_BASE + (uint32_t)(c & 1) * SLOT;
-#pragma unroll
-    for (int j = 0; j < SC_LINES; ++j) {
-      const uint32_t line = wave * SC_LINES + j;
-      const bool is_w = line < BN / 32;
-      const uint32_t row0 = (is_w ? line : line - BN / 32) * 32;
-      load_line_to_lds(is_w ? rsw : rsa, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
-    }
-  };
-  auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
-  auto read_scales = [&](int w, uint32_t (&scw)[4], uint32_t (&sca)[2]) {
-    if constexpr (HAS_SC) {
-      const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
-      const uint32_t g = lane >> 5, r32 = lane & 31;
-      const uint32_t col = (uint32_t)(w % CW) * SC_WIN + ((SC_WIN == 8) ? 4 * g : 0);
-      const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * g;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        scw[i] = *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i + r32) * SC_ROW + col) >> sh;
-      if constexpr (MODE == GEMM_W4A4) {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          sca[j] = *reinterpret_cast<const uint32_t*>(slot + (BN + wm * 64 + 32 * j + r32) * SC_ROW + col) >> sh;
-      }
-    }
+  auto issue_w = [&](int w, int j) {
+    const uint32_t line = wave * LINES + j;
+    load_line_to_lds(rw, w_slot(w) + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+                     (uint32_t)w * RB + line * ROWS_PER_LINE * p.w_row_bytes);
   };
 
-  v16f acc[4][2];
+  v4f acc[4][8];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 8; ++j)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+      for (int e = 0; e < 4; ++e) acc[i][j][e] = 0.0f;
+  v4i f0[12], f1[12];
+  constexpr int RD = 12;                              // ds_read_b128 per fragment set
+  constexpr int VM = 2 * LINES;                       // tile loads after each hand-over
 
-  const int nwin = p.nwin;
-  uint32_t scw[4] = {0, 0, 0, 0}, sca[2] = {0, 0};
-  v4i f0[8], f1[8];
-  constexpr int RD = (MODE == GEMM_W4A8) ? 8 : 6;        // ds_read_b128 per fragment set
-  constexpr int VM = A_LINES + W_LINES;
-  constexpr int VM1 = SPLIT ? A_LINES : W_LINES, VM0 = SPLIT ? W_LINES : A_LINES;
-  constexpr int WAIT_VM = SPLIT ? A_LINES : (NA - 2) * VM;
-
-  issue_loads(0);
-  if constexpr (HAS_SC) issue_chunk(0);
+  // prologue: window 0 resident; then, in the order the steady state issues them, the
+  // activation tile of window 1, the weight tile of window 1, the activation tile of window 2
+#pragma unroll
+  for (int j = 0; j < LINES; ++j) {
+    issue_a(0, j);
+    issue_w(0, j);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if constexpr (HAS_SC)
-    if (nchunks > 1) issue_chunk(1);
 #pragma unroll
-  for (int k = 1; k < (SPLIT ? 2 : NS); ++k)
-    if (k < nwin) issue_loads(k);
-  read_frags8<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
-  read_scales(0, scw, sca);
+  for (int j = 0; j < LINES; ++j) issue_a(1, j);
+#pragma unroll
+  for (int j = 0; j < LINES; ++j) issue_w(1, j);
+#pragma unroll
+  for (int j = 0; j < LINES; ++j) issue_a(2, j);
+  read_frags_bf16(f0, a_slot(0), w_slot(0), wm, wn, lane, 0, [](int) {});
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  auto window = [&](int w, auto pend_tag, auto steady_tag) {
-    constexpr bool PEND = decltype(pend_tag)::value;
-    constexpr bool STEADY = decltype(steady_tag)::value;
-    const uint8_t* la = a_slot(w);
-    const uint8_t* lw = w_slot(w);
-    if constexpr (HAS_SC)
-      if (chunk_due(w)) issue_chunk(w / CW + 1);
+  // One window: step 0 on f0 under the reads of step 1 into f1; the hand-over waits for
+  // window w+1 (only the activation tile of window w+2 may still be in flight) and
+  // releases window w's slots; step 1 on f1 under the reads of window w+1's step 0 into
+  // f0 and the DMA of the weight tile of window w+2 and the activation tile of window
+  // w+3.  Every window refills, the last ones with tiles past K: buffer loads that stay
+  // inside each resource (bytes of later rows, or zeros past its end) into slots no later
+  // window reads.  A single loop body keeps the register allocator from splitting the
+  // 32 accumulators between loop copies.
+  const int nwin = p.nwin;
+  for (int w = 0; w < nwin; ++w) {
+    read_frags_bf16(f1, a_slot(w), w_slot(w), wm, wn, lane, 1, [](int) {});
+    mfma_bf16_step(acc, f0);
+    sched_units<0, RD, 32, 0, false>(std::make_integer_sequence<int, RD>{});
     __builtin_amdgcn_sched_barrier(0);
-    auto pend_loads = [&](int k) {
-      if constexpr (PEND) {
-        if (dma_after(k, VM1, RD) > 0) {
-          if constexpr (SPLIT)
-            issue_line(w + NA - 1, I0{}, k * VM1 / RD);
-          else
-            issue_line(w + NS - 1, I1{}, k * VM1 / RD);
-        }
-      }
-    };
-    uint32_t scw_n[4], sca_n[2];
-    if constexpr (C::STEPS == 4) {
-      read_frags8<MODE>(f1, la, lw, wm, wn, lane, 1, pend_loads);
-      mfma8<MODE, 0>(acc, f0, scw, sca);
-      interleave8<RD, PEND ? VM1 : 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags8<MODE>(f0, la, lw, wm, wn, lane, 2);
-      read_scales(w + 1, scw_n, sca_n);
-      mfma8<MODE, 1>(acc, f1, scw, sca);
-      interleave8<RD + (HAS_SC ? 4 : 0) + (MODE == GEMM_W4A4 ? 2 : 0), 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags8<MODE>(f1, la, lw, wm, wn, lane, 3);
-      mfma8<MODE, 2>(acc, f0, scw, sca);
-      interleave8<RD, 0>();
-    } else {
-      read_frags8<MODE>(f1, la, lw, wm, wn, lane, 1, pend_loads);
-      read_scales(w + 1, scw_n, sca_n);
-      mfma8<MODE, 0>(acc, f0, scw, sca);
-      interleave8<RD + (HAS_SC ? 4 : 0), PEND ? VM1 : 0>();
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if constexpr (STEADY && WAIT_VM > 0)
-      __builtin_amdgcn_s_waitcnt(waitcnt_vm(WAIT_VM));
-    else
-      __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(LINES));   // window w+1 landed
     stage_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    read_frags8<MODE>(f0, a_slot(w + 1), w_slot(w + 1), wm, wn, lane, 0, [&](int k) {
-      if constexpr (STEADY) {
-        if (dma_after(k, VM0, RD) > 0) {
-          if constexpr (SPLIT)
-            issue_line(w + NW, I1{}, k * VM0 / RD);
-          else
-            issue_line(w + NS, I0{}, k * VM0 / RD);
-        }
+    read_frags_bf16(f0, a_slot(w + 1), w_slot(w + 1), wm, wn, lane, 0, [&](int k) {
+      if (dma_after(k, VM, RD) > 0) {
+        const int j = k * VM / RD;
+        if (j < LINES)
+          issue_w(w + NW, j);
+        else
+          issue_a(w + NA, j - LINES);
       }
     });
-    if constexpr (C::STEPS == 4)
-      mfma8<MODE, 3>(acc, f1, scw, sca);
-    else
-      mfma8<MODE, 1>(acc, f1, scw, sca);
-    interleave8<RD, STEADY ? VM0 : 0>();
+    mfma_bf16_step(acc, f1);
+    sched_units<1, RD, 32, VM, true>(std::make_integer_sequence<int, RD>{});
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) scw[i] = scw_n[i];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) sca[j] = sca_n[j];
-  };
-  using T_ = std::true_type;
-  using F_ = std::false_type;
-  int w = 0;
-  if constexpr (SPLIT) {
-    for (; w < nwin - 2; ++w) window(w, T_{}, T_{});
-  } else if (nwin > NS) {
-    window(0, F_{}, T_{});
-    for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{});
-    window(w, T_{}, F_{});
-    ++w;
   }
-  for (; w < nwin; ++w) window(w, F_{}, F_{});
 
-  // ---- epilogue: fp32 -> bf16 (RNE) ----
-  const uint32_t r32 = lane & 31, g = lane >> 5;
+  // ---- epilogue: fp32 -> bf16 (RNE); lane l holds columns 4g .. 4g+3 of row l & 15 of
+  // every 16 x 16 block ----
+  const uint32_t r16 = lane & 15, g = lane >> 4;
   if (p.vec16 && n0 + BN <= p.N) {
-    // each wave parks its 64 x 128 sub-tile in its own 16 KB of LDS (16-byte chunk c of
-    // row r at slot c ^ (r & 15)) and stores 4 whole 256-byte row segments per instruction
+    // park the wave's 128 (m) x 64 (n) sub-tile in LDS (16-byte chunk c of row r at
+    // c ^ (r & 7)) and store whole 128-byte row segments; the loop's last loads are waited
+    // for by the barrier's release fence before any wave overwrites the rings
     __syncthreads();
-    uint8_t* sub = lds + wave * (64u * 256u);
+    uint8_t* sub = lds + wave * (128u * 128u);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t row = 32 * j + r32;
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t row = 16 * j + r16;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
-          float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
-          if constexpr (MODE == GEMM_W4A8) {
-            v0 *= p.a_scale;
-            v1 *= p.a_scale;
-            v2 *= p.a_scale;
-            v3 *= p.a_scale;
-          }
-          const uint32_t chunk = 4 * i + pp;
-          *reinterpret_cast<v2u*>(sub + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * g) =
-              v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        }
+      for (int i = 0; i < 4; ++i) {
+        const v4f& v = acc[i][j];
+        const uint32_t chunk = 2 * i + (g >> 1);
+        *reinterpret_cast<v2u*>(sub + row * 128 + ((chunk ^ (row & 7)) << 4) + 8 * (g & 1)) =
+            v2u{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      }
     }
-    const int mw = m0 + (int)wm * 64;
-    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
+    const int mw = m0 + (int)wm * 128;
+    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 64;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
-      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
+      const uint32_t row = 8 * q + (lane >> 3), c = lane & 7;
+      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 128 + ((c ^ (row & 7)) << 4));
       if (mw + (int)row < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)row * p.ld_out + c * 8) = v;
     }
     return;
   }
+  // partial column tiles: a lane owns 4 consecutive columns per store
   const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int m = m0 + (int)(wm * 64 + 32 * j + r32);
+  for (int j = 0; j < 8; ++j) {
+    const int m = m0 + (int)(wm * 128 + 16 * j + r16);
     uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
-        float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
-        float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
-        if constexpr (MODE == GEMM_W4A8) {
-          v0 *= p.a_scale;
-          v1 *= p.a_scale;
-          v2 *= p.a_scale;
-          v3 *= p.a_scale;
-        }
-        const unsigned lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
-        if (full) {
+      const int n = n0 + (int)(wn * 64 + 16 * i + 4 * g);
+      const v4f& v = acc[i][j];
+      const unsigned lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+      if (full) {
+        *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+      } else if (m < p.M) {
+        if (p.vec_store && n + 4 <= p.N) {
           *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
-        } else if (m < p.M) {
-          if (p.vec_store && n + 4 <= p.N) {
-            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
-          } else {
-            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
-            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
-            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
-            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
-          }
+        } else {
+          if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
+          if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
+          if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
+          if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
         }
       }
     }
@@ -1494,9 +1332,12 @@ __device__ __forceinline__ void mx_quad4_convert_bf16(const v4i (&d)[4], int sca
 }
 
 // Fast fused kernel (bf16 activations; K a whole number of 256-element windows; weight
-// scale rows and planes on 16-byte boundaries), eight waves: the MFMA layout and weight
-// streaming of gemm_fast8_kernel<GEMM_W4A4> (wave = 64 x 128 sub-tile; two-slot weight
-// ring; 32-byte weight scale chunks), and the activation tile quantized in the kernel.
+// scale rows and planes on 16-byte boundaries), eight waves (two per SIMD).  Each wave
+// owns a 64 (m) x 128 (n) sub-tile: 4 weight x 2 activation fragments of 32x32x64 MFMAs,
+// 8 accumulators; every 32 x 32 output block gets the same MFMAs in the same order as in
+// gemm_fast_kernel<GEMM_W4A4>, hence the same bits.  Weight tiles stream through a
+// two-slot ring with 32-byte weight scale chunks; the activation tile is quantized in the
+// kernel.
 // Activation window w+1 is quantized during window w, a quarter per MFMA step: wave v
 // quantizes rows 32v + 8q .. +7 of quarter q from registers loaded D steps earlier (1 KB =
 // 2 rows x 256 elements per load instruction, 4 per quarter), and writes 4 code bytes per
@@ -1505,6 +1346,8 @@ __device__ __forceinline__ void mx_quad4_convert_bf16(const v4i (&d)[4], int sca
 // quantized after the hand-over barrier of window w-1, which releases its slot; quarters
 // 1-3 under steps 0-2 of window w.  A step runs as two units in source order, fenced
 // from each other: 4 MFMAs, 3 fragment reads and half of the quantization each.
+constexpr int NT8 = 512;
+
 template <bool UOS, int D>
 __global__ __launch_bounds__(NT8, 1) void gemm_w4a4_fused8_kernel(Params p) {
   static_assert(D == 1 || D == 2 || D == 4, "load lead of 1, 2 or 4 steps");
@@ -1825,11 +1668,11 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
     p.w_row_bytes = w_row_bytes;
     if (K > 0 && K % Fast<MD>::K_WIN == 0 && (scales_ok || !needs_scales)) {
       p.nwin = (int)(K / Fast<MD>::K_WIN);
-      // the bf16 reference runs two waves per SIMD (measured faster); the scaled modes one
-      // (measured slower with two: 64 x 128 wave tiles read half again as many fragments
-      // per MFMA)
+      // the bf16 reference runs its 16 x 16 eight-wave kernel; the scaled modes the
+      // four-wave 32 x 32 kernel, whose W4A4 MFMA order the fused kernel reproduces bit
+      // for bit (eight waves of 32 x 32 MFMAs measured slower for both scaled modes)
       if constexpr (MD == GEMM_BF16)
-        hipLaunchKernelGGL(gemm_fast8_kernel<MD>, grid, dim3(NT8), 0, stream, p);
+        hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(NT16), 0, stream, p);
       else
         hipLaunchKernelGGL(gemm_fast_kernel<MD>, grid, block, 0, stream, p);
     } else {
