@@ -15,8 +15,9 @@ static FP8 scale is calibrated once, before timing):
 
 Prints ONE JSON line.  `value` is the step's GEMM throughput (all GEMM FLOPs of the step
 divided by the step time, TFLOP/s).  `roofline` describes the kernel that takes the most
-time; `kernels` gives every kernel's achieved rate against its own roofline, all timed
-with HIP events on the stream the kernels run on.  `cpu_baseline` times the CPU oracle
+time; `kernels` gives every kernel's achieved rate (from its mean time over the steps;
+median, standard deviation and coefficient of variation beside it) against its own
+roofline, all timed with HIP events on the stream the kernels run on.  `cpu_baseline` times the CPU oracle
 on a bounded row sample of the same workload.
 """
 
@@ -187,8 +188,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    per_kernel_ms = {name: float(np.mean([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)]))
-                     for i, (name, _) in enumerate(kernels)}
+    samples = {name: np.array([ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps)])
+               for i, (name, _) in enumerate(kernels)}
+    per_kernel_ms = {name: float(np.mean(t)) for name, t in samples.items()}
     step_ms = float(np.mean([ev[s][0].elapsed_time(ev[s][-1]) for s in range(args.steps)]))
     ms_per_step = wall * 1e3 / args.steps
 
@@ -200,7 +202,10 @@ def main():
         amount, unit, peak, bound = work[name]
         rate = amount / (ms * 1e-3) / (1e12 if unit == "TFLOP/s" else 1e9)
         prof_name = "mxq_sqnr" if name.startswith("mxq_sqnr") else name
-        kinfo[name] = {"ms": round(ms, 4), "achieved": round(rate, 2), "unit": unit, "peak": peak,
+        t = samples[name]
+        kinfo[name] = {"ms": round(ms, 4), "median_ms": round(float(np.median(t)), 4),
+                       "std_ms": round(float(np.std(t)), 4), "cv": round(float(np.std(t) / ms), 4),
+                       "achieved": round(rate, 2), "unit": unit, "peak": peak,
                        "frac": round(rate / peak, 4), "bound": bound,
                        "traffic": _traffic_from_profile(f"{prof_name}_{args.workload}", _src_hash(*src_keys[name]))}
     dominant = max(per_kernel_ms, key=per_kernel_ms.get)
