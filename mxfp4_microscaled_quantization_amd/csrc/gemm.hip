@@ -368,16 +368,12 @@ __global__ __launch_bounds__(NT, 1) void gemm_generic_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------------
-// Fast path: K is a whole number of windows and scale rows are 4-byte multiples (every
-// workload shape).  Tiles stream global -> LDS with buffer_load ... lds (no staging
-// registers); each wave issues whole 1 KB LDS lines whose lanes fetch the chunk the XOR
-// swizzle places there.  One barrier per window; the next window's loads and its first
-// fragment reads are issued under the current window's last MFMA step.
-// buffer_load_dword ... lds: 4 bytes per lane into LDS at `lds_line` + 4 * lane
-__device__ __forceinline__ void load_dword_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_line, uint32_t voff,
-                                                  uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_line, 4, voff, soff, 0, 0);
-}
+// Fast path: K is a whole number of windows, and scale rows are 16-byte multiples on
+// 16-byte aligned planes (every workload shape).  Tiles stream global -> LDS with
+// buffer_load ... lds (no staging registers); each wave issues whole 1 KB LDS lines whose
+// lanes fetch the chunk the XOR swizzle places there.  One barrier per window; the next
+// window's loads and its first fragment reads are issued under the current window's last
+// MFMA step.
 
 // buffer_load_dwordx4 ... lds: 16 bytes per lane into LDS at `lds_line` + 16 * lane
 __device__ __forceinline__ void load_line_to_lds(__amdgpu_buffer_rsrc_t r, uint8_t* lds_line, uint32_t voff,
@@ -619,8 +615,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // One window.  PEND: the step-0 tile loads go out (the weight tile of window w+NS-1,
   // whose activation tile went out at the previous hand-over).  STEADY: the hand-over
   // waits for window w+1 only and refills the slot this window releases with the
-  // activation tile of window w+NS.  The tail waits for everything and loads no tiles.  Memory-free MFMAs cannot be sunk past the barrier: every step is its
-  // own scheduling region.
+  // activation tile of window w+NS.  The tail waits for everything and loads no tiles.
+  // Memory-free MFMAs cannot be sunk past the barrier: every step is its own scheduling
+  // region.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   auto window = [&](int w, auto pend_tag, auto steady_tag) {
