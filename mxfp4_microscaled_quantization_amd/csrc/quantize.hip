@@ -28,13 +28,9 @@
 namespace mxq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kUnroll = 4;            // blocks in flight per quad
-constexpr int kBlocksPerIter = kThreads / 4 * kUnroll;
-// mx_quantize_kernel: larger workgroups and more blocks in flight per quad measured best
-// for it (77 % of HBM against 63 % with the settings above); the rotated quantizer keeps
-// the settings above (its butterfly holds more registers per block), and the FP8 kernel
-// runs 1024-thread workgroups.
+constexpr int kThreads = 256;         // absmax_kernel
+// mx_quantize_kernel: 512-thread workgroups, 8 blocks in flight per quad (77 % of HBM
+// against 63 % with 256 threads and 4 blocks); the FP8 kernel runs 1024-thread workgroups.
 constexpr int kMxThreads = 512;
 constexpr int kMxUnroll = 8;
 constexpr int kMxBlocksPerIter = kMxThreads / 4 * kMxUnroll;
@@ -44,6 +40,11 @@ constexpr int kFp8Unroll = 2;     // chunks of 16 per lane per pass (72 % of HBM
 // HBM against 58 % for one quarter per lane and 256 threads)
 constexpr int kDqThreads = 512;
 constexpr int kDqUnroll = 8;
+// mx_quantize_rot_kernel: 512-thread workgroups, 4 blocks in flight per quad, every load
+// of an iteration issued before its butterflies (66 % of HBM for n = 64 against 61 % with
+// 256 threads and each block's load, butterfly and store in turn)
+constexpr int kRotThreads = 512;
+constexpr int kRotUnroll = 4;
 
 __device__ __forceinline__ float lo_f32(int pair) { return __uint_as_float((unsigned)pair << 16); }
 __device__ __forceinline__ float hi_f32(int pair) { return __uint_as_float((unsigned)pair & 0xFFFF0000u); }
@@ -167,59 +168,72 @@ __device__ __forceinline__ float lane_xor(float v, int lane) {
   } else if constexpr (D == 8) {
     return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));   // row_ror:8
   } else {
+    // through the LDS crossbar (ds_bpermute): measured faster here than the gfx950
+    // v_permlane16_swap, whose operand copies and hazard waits serialize the exchanges
     return __shfl_xor(v, D);
   }
 }
 
-template <bool F32, int N, bool UOS>
-__global__ __launch_bounds__(kThreads) void mx_quantize_rot_kernel(
+template <bool F32, int N, bool UOS, int THREADS, int UNROLL>
+__global__ __launch_bounds__(THREADS) void mx_quantize_rot_kernel(
     const void* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ codes, int64_t ld_codes,
     uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks,
     int contiguous) {
   static_assert(N == 16 || N == 64 || N == 256, "rotation runs of 16, 64 or 256");
   constexpr float kNorm = N == 16 ? 0.25f : (N == 64 ? 0.125f : 0.0625f);   // 1 / sqrt(N)
+  constexpr int BLOCKS_PER_ITER = THREADS / 4 * UNROLL;
   const int tid = threadIdx.x;
   const int q = tid & 3;
   const int lane = tid & 63;
-  const int64_t stride = (int64_t)gridDim.x * kBlocksPerIter;
-  for (int64_t base = (int64_t)blockIdx.x * kBlocksPerIter; base < total_blocks; base += stride) {
+  const int64_t stride = (int64_t)gridDim.x * BLOCKS_PER_ITER;
+  for (int64_t base = (int64_t)blockIdx.x * BLOCKS_PER_ITER; base < total_blocks; base += stride) {
+    // every block's loads first, then the butterflies and stores
+    int64_t co[UNROLL], so[UNROLL];
+    bool ok[UNROLL];
+    v4i d0[UNROLL], d1[UNROLL];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int64_t b = base + u * (kThreads / 4) + (tid >> 2);
-      const bool ok = b < total_blocks;
-      int64_t xo, co, so;
+    for (int u = 0; u < UNROLL; ++u) {
+      const int64_t b = base + u * (THREADS / 4) + (tid >> 2);
+      ok[u] = b < total_blocks;
+      int64_t xo;
       if (contiguous) {
         xo = b * 32 + q * 8;
-        co = b * 16 + q * 4;
-        so = b;
+        co[u] = b * 16 + q * 4;
+        so[u] = b;
       } else {
         const uint32_t bb = (uint32_t)b;
         const uint32_t row = bb / blocks_per_row;
         const uint32_t blk = bb - row * blocks_per_row;
         xo = (int64_t)row * ld_x + blk * 32 + q * 8;
-        co = (int64_t)row * ld_codes + blk * 16 + q * 4;
-        so = (int64_t)row * ld_scales + blk;
+        co[u] = (int64_t)row * ld_codes + blk * 16 + q * 4;
+        so[u] = (int64_t)row * ld_scales + blk;
       }
+      d0[u] = v4i{0, 0, 0, 0};
+      d1[u] = v4i{0, 0, 0, 0};
+      if (ok[u]) {
+        if (F32) {
+          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
+          d0[u] = __builtin_nontemporal_load(p);
+          d1[u] = __builtin_nontemporal_load(p + 1);
+        } else {
+          d0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo));
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UNROLL; ++u) {
       float v[8];
       if (F32) {
-        v4i d0 = v4i{0, 0, 0, 0}, d1 = v4i{0, 0, 0, 0};
-        if (ok) {
-          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
-          d0 = __builtin_nontemporal_load(p);
-          d1 = __builtin_nontemporal_load(p + 1);
-        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] = __int_as_float(d0[i]);
-          v[4 + i] = __int_as_float(d1[i]);
+          v[i] = __int_as_float(d0[u][i]);
+          v[4 + i] = __int_as_float(d1[u][i]);
         }
       } else {
-        v4i d0 = v4i{0, 0, 0, 0};
-        if (ok) d0 = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[2 * i] = lo_f32(d0[i]);
-          v[2 * i + 1] = hi_f32(d0[i]);
+          v[2 * i] = lo_f32(d0[u][i]);
+          v[2 * i + 1] = hi_f32(d0[u][i]);
         }
       }
       // stages h = 1, 2, 4 inside the lane
@@ -264,9 +278,9 @@ __global__ __launch_bounds__(kThreads) void mx_quantize_rot_kernel(
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
       r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
-      if (ok) {
-        *reinterpret_cast<unsigned*>(codes + co) = r;
-        if (q == 0) scales[so] = (uint8_t)s;
+      if (ok[u]) {
+        __builtin_nontemporal_store(r, reinterpret_cast<unsigned*>(codes + co[u]));
+        if (q == 0) scales[so[u]] = (uint8_t)s;
       }
     }
   }
@@ -477,15 +491,16 @@ hipError_t launch_quantize_mxfp4_rotated(const void* x, bool f32, int64_t rows, 
   const int64_t total = rows * bpr;
   if (total == 0) return hipSuccess;
   const int contiguous = (ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr) ? 1 : 0;
-  const int grid = grid_for(total, kBlocksPerIter);
+  constexpr int T = kRotThreads, U = kRotUnroll;
+  const int grid = grid_for(total, T / 4 * U);
   auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(kThreads), 0, stream, x, ld_x, codes, ld_codes, scales, ld_scales,
+    hipLaunchKernelGGL(kernel, dim3(grid), dim3(T), 0, stream, x, ld_x, codes, ld_codes, scales, ld_scales,
                        (uint32_t)bpr, total, contiguous);
   };
   auto pick_rule = [&](auto f32_tag, auto n_tag) {
     constexpr bool F = decltype(f32_tag)::value;
     constexpr int NN = decltype(n_tag)::value;
-    uos ? go(mx_quantize_rot_kernel<F, NN, true>) : go(mx_quantize_rot_kernel<F, NN, false>);
+    uos ? go(mx_quantize_rot_kernel<F, NN, true, T, U>) : go(mx_quantize_rot_kernel<F, NN, false, T, U>);
   };
   auto pick_n = [&](auto f32_tag) {
     if (n == 16)
