@@ -61,7 +61,7 @@ extern "C" {
 typedef enum {
   MXQ_OK = 0,
   MXQ_ERR_INVALID_ARG = 1, /* bad size, pointer, alignment or leading dimension */
-  MXQ_ERR_UNSUPPORTED = 2, /* valid request this build cannot serve (e.g. unknown dtype) */
+  MXQ_ERR_UNSUPPORTED = 2, /* well-formed request the library does not serve (e.g. unknown dtype) */
   MXQ_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
 } mxq_status;
 
