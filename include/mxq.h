@@ -25,7 +25,8 @@
  * Conventions for every entry point:
  *  - Pointers are DEVICE pointers (HBM) owned by the caller; the library never
  *    allocates, frees or retains them.  Scalars are passed by value.  The one
- *    host-visible result (mxq_sqnr's three doubles) is written to device memory.
+ *    host-visible result (mxq_sqnr's three doubles) is written to device memory.  The
+ *    exception is mxq_fp8_static_scales, a host computation on host pointers.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Every call only enqueues
  *    work on it and returns; nothing synchronizes.  Device-side faults surface at the
  *    caller's next synchronization.
@@ -126,6 +127,7 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int6
  *   E4M3 round-to-nearest-even saturating at +-448 (never NaN); sign bit from the product.
  * inv_scale is the static per-tensor multiplier, normally fl32(448 / amax) with amax
  * measured once ahead of time (mxq_absmax); the GEMM takes s_a = fl32(amax / 448).
+ * mxq_fp8_static_scales forms both.
  * x : rows x cols of `dt`, pitch ld_x elements; base and pitch 16-byte aligned.
  * q : out, rows x cols bytes, pitch ld_q bytes; base and pitch multiples of 16.
  * cols must be a multiple of 16.  Errors as for mxq_quantize; inv_scale must be finite
@@ -133,6 +135,19 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int6
  */
 mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                             float inv_scale, uint8_t* q, int64_t ld_q, void* stream);
+
+/*
+ * mxq_fp8_static_scales -- the static per-tensor scales of FP8 E4M3 activations ([Q13]:
+ * W4A8 takes static FP8 E4M3 activations; the per-tensor amax is mapped onto the largest
+ * finite E4M3 value, 448):
+ *   *s_a   = fl32(amax / 448)  -- the dequantization scale mxq_gemm_w4a8 takes (a_scale),
+ *   *inv_s = fl32(448 / amax)  -- the multiplier mxq_quantize_fp8 takes (inv_scale),
+ * each the binary32 quotient rounded to nearest even.  A host function: amax is a value,
+ * s_a and inv_s are HOST pointers written only on success; nothing touches the GPU.
+ * Errors: NULL s_a / inv_s, amax not finite or <= 0, or 448 / amax beyond binary32's
+ * range (amax below 448 / FLT_MAX) -> MXQ_ERR_INVALID_ARG.
+ */
+mxq_status mxq_fp8_static_scales(float amax, float* s_a, float* inv_s);
 
 /*
  * mxq_absmax -- max |x| over a rows x cols tensor, written as one float to *out (device).
@@ -199,8 +214,9 @@ mxq_status mxq_gemm_bf16(const uint16_t* a, const uint16_t* w, int64_t M, int64_
  * mxq_sqnr -- whole-output SQNR of `test` against `ref` ([Q13] block-output SQNR):
  *   S = sum ref^2, N = sum (ref - test)^2 over all rows x cols bf16 elements (exactly
  *   widened), dB = 10 log10(S / N); N == 0 -> +inf, S == N == 0 -> NaN.
- * Deterministic: fixed partition, per-thread fp32 -> per-workgroup fp64 -> one final
- * fp64 pass.  workspace: device scratch of at least mxq_sqnr_workspace_bytes(rows*cols)
+ * Deterministic: fixed partition; every value widened exactly and every difference,
+ * square and sum formed in fp64 (per thread -> per workgroup -> one final pass), so
+ * any finite bf16 inputs are in range.  workspace: device scratch of at least mxq_sqnr_workspace_bytes(rows*cols)
  * bytes (8-byte aligned), owned by the caller.  out3: device double[3] = {S, N, dB}.
  * ref/test pitches in elements; bases 16-byte aligned, pitches multiples of 8, cols % 8 == 0.
  */
@@ -219,6 +235,20 @@ mxq_status mxq_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int
 mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                           int64_t ld_scales, int64_t rows, int64_t cols, uint16_t* y,
                           int64_t ld_y, void* stream);
+
+/*
+ * mxq_dequantize_fp8 -- FP8 E4M3 -> bf16, the W4A8 activation half of quantize-dequantize
+ * (QDQ) emulation ([Q13]: W4A8 quality was measured by QDQ emulation):
+ *   y = bf16_RNE( fl32( e4m3(q) * a_scale ) )
+ * i.e. the exact E4M3 value times the static dequantization scale s_a in one binary32
+ * multiply (round to nearest even), then rounded to bf16 (nearest even).  NaN codes
+ * (S.1111.111, which mxq_quantize_fp8 never writes) give NaN.
+ * q : rows x cols bytes, pitch ld_q bytes; base and pitch multiples of 16.
+ * y : out, rows x cols bf16, pitch ld_y elements; base 16-byte aligned, ld_y % 8 == 0.
+ * cols % 16 == 0; a_scale finite.  Errors -> MXQ_ERR_INVALID_ARG before any launch.
+ */
+mxq_status mxq_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int64_t rows, int64_t cols,
+                              uint16_t* y, int64_t ld_y, void* stream);
 
 /*
  * Measurement aid (not part of the quantize / GEMM path).

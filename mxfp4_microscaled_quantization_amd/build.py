@@ -4,13 +4,15 @@
 
 (run as a script: importing the package would load the library being rebuilt)
 
-All HIP sources under csrc/ are compiled into one shared library next to this file.
+All HIP sources under csrc/ are compiled (in parallel) and linked into one shared library
+next to this file; objects go to _build/.
 Packed-FP32 VALU instructions are disabled (-packed-fp32-ops); no fast-math.
 """
 
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -32,21 +34,43 @@ def hipcc() -> str:
     return cand if os.path.exists(cand) else "hipcc"
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source into libmxq.so (always rebuilds); returns its path."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *FLAGS, *extra_flags, "-o", tmp, *srcs]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    res = subprocess.run(cmd, capture_output=True, text=True)
+def _filter(text: str):
     # hipcc's host pass reports the device-only feature flag as unknown: harmless
     noise = ("packed-fp32-ops", "unknown target feature", "-target-feature")
-    msgs = [ln for ln in (res.stdout + res.stderr).splitlines() if ln and not any(n in ln for n in noise)]
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
+    return [ln for ln in text.splitlines() if ln and not any(n in ln for n in noise)]
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every HIP source into libmxq.so (always rebuilds); returns its path.
+
+    Each source is compiled to an object in parallel (no device code crosses a source
+    file), then the objects are linked into the shared library."""
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    compile_flags = [f for f in FLAGS if f != "-shared"]
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
+        cmd = [hipcc(), *compile_flags, *extra_flags, "-c", "-o", obj, os.path.join(CSRC, src)]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        return obj, res
+
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        results = list(ex.map(compile_one, SOURCES))
+    msgs = []
+    for obj, res in results:
+        msgs += _filter(res.stdout + res.stderr)
+        if res.returncode != 0:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
+    tmp = LIB + ".tmp"
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *[o for o, _ in results]]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("link failed:\n" + "\n".join(_filter(res.stdout + res.stderr)))
     # a kernel whose host stub was not emitted leaves an undefined symbol behind
     und = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True).stdout
     bad = [ln for ln in und.splitlines() if "__device_stub__" in ln]

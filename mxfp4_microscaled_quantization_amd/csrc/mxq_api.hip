@@ -1,6 +1,7 @@
 // C ABI of libmxq: argument validation, error reporting and dispatch to the gfx950
 // launchers.  Every check runs before anything is enqueued, so an error return means the
 // stream was not touched.  The only mutable state is the thread-local error message.
+#include <float.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <string.h>
@@ -163,6 +164,22 @@ mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t c
                                                  as_stream(stream)));
 }
 
+mxq_status mxq_fp8_static_scales(float amax, float* s_a, float* inv_s) {
+  const char* fn = "mxq_fp8_static_scales";
+  if (!s_a || !inv_s) return fail(MXQ_ERR_INVALID_ARG, "%s: s_a/inv_s is NULL", fn);
+  if (!(amax > 0.0f) || !(amax <= FLT_MAX))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: amax must be finite and > 0 (got %g)", fn, (double)amax);
+  // IEEE binary32 division rounds the exact quotient to nearest even: fl32(amax / 448)
+  // and fl32(448 / amax)
+  const float sa = amax / 448.0f;
+  const float inv = 448.0f / amax;
+  if (!(inv <= FLT_MAX))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: amax (%g) too small: 448 / amax overflows binary32", fn, (double)amax);
+  *s_a = sa;
+  *inv_s = inv;
+  return ok();
+}
+
 mxq_status mxq_absmax(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x, float* out,
                       void* stream) {
   const char* fn = "mxq_absmax";
@@ -277,6 +294,25 @@ mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t*
   }
   return hip_status(fn, mxq::launch_dequantize(codes, ld_codes, scales, ld_scales, rows, cols, y, ld_y,
                                                as_stream(stream)));
+}
+
+mxq_status mxq_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int64_t rows, int64_t cols,
+                              uint16_t* y, int64_t ld_y, void* stream) {
+  const char* fn = "mxq_dequantize_fp8";
+  if (rows < 0 || cols < 0) return fail(MXQ_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (cols % 16 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 16", fn, (long long)cols);
+  if (ld_q < cols || ld_y < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below the row width", fn);
+  if (!(a_scale == a_scale) || a_scale == __builtin_inff() || a_scale == -__builtin_inff())
+    return fail(MXQ_ERR_INVALID_ARG, "%s: a_scale must be finite", fn);
+  if (rows > (int64_t)0x7FFFFFFF || rows * (cols / 8) >= ((int64_t)1 << 32))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  if (rows > 0 && cols > 0) {
+    if (!q || !y) return fail(MXQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
+    if (!aligned(q, 16) || ld_q % 16 != 0)
+      return fail(MXQ_ERR_INVALID_ARG, "%s: q base and ld_q must be multiples of 16 bytes", fn);
+    if (!aligned(y, 16) || ld_y % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: y base and pitch must be 16-byte aligned", fn);
+  }
+  return hip_status(fn, mxq::launch_dequantize_fp8(q, ld_q, a_scale, rows, cols, y, ld_y, as_stream(stream)));
 }
 
 mxq_status mxq_mfma_ceiling(mxq_gemm_mode mode, const void* a, const uint8_t* a_scales, const void* w,

@@ -21,6 +21,8 @@ hipError_t launch_absmax(const void* x, bool f32, int64_t rows, int64_t cols, in
 hipError_t launch_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales,
                              int64_t ld_scales, int64_t rows, int64_t cols, uint16_t* y, int64_t ld_y,
                              hipStream_t stream);
+hipError_t launch_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int64_t rows, int64_t cols,
+                                 uint16_t* y, int64_t ld_y, hipStream_t stream);
 
 enum GemmMode { GEMM_W4A4 = 0, GEMM_W4A8 = 1, GEMM_BF16 = 2 };
 hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,

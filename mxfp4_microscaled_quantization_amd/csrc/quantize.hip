@@ -1,5 +1,6 @@
 // Bandwidth-bound element kernels for gfx950: MXFP4 block quantization, static FP8 E4M3
-// quantization, absolute maximum (static-scale calibration) and MXFP4 dequantization.
+// quantization, absolute maximum (static-scale calibration), and MXFP4 and FP8 E4M3
+// dequantization (the quantize-dequantize emulation steps).
 //
 // MXFP4 rule ("AMD Quark: 1.92x faster FLUX.1-dev with MXFP4 on Instinct MI350", section
 // "What is MXFP4": 32-element blocks share one scale; "MXAttention ...", section "What it
@@ -40,6 +41,10 @@ constexpr int kFp8Unroll = 2;     // chunks of 16 per lane per pass (72 % of HBM
 // HBM against 58 % for one quarter per lane and 256 threads)
 constexpr int kDqThreads = 512;
 constexpr int kDqUnroll = 8;
+// dequantize_fp8_kernel: 8 codes (8 bytes in, 16 bytes out) per lane per unit, 4 units
+// per lane per pass, loads first
+constexpr int kDq8Threads = 512;
+constexpr int kDq8Unroll = 4;
 // mx_quantize_rot_kernel: 512-thread workgroups, 4 blocks in flight per quad, every load
 // of an iteration issued before its butterflies (66 % of HBM for n = 64 against 61 % with
 // 256 threads and each block's load, butterfly and store in turn)
@@ -463,6 +468,46 @@ int grid_for(int64_t work_items, int64_t per_block) {
   return (int)(g < 1 ? 1 : g);
 }
 
+
+// ---------------------------------------------------------------------------------
+// FP8 E4M3 -> bf16 dequantization of statically scaled activations: y = bf16_RNE(
+// fl32(e4m3(q) * a_scale)).  v_cvt_pk_f32_fp8 widens two OCP E4M3 bytes exactly to
+// binary32 (NaN for S.1111.111); the product is one binary32 multiply; v_cvt_pk_bf16_f32
+// rounds to nearest even.  A lane owns 8 consecutive codes of a row per unit.
+__global__ __launch_bounds__(kDq8Threads) void dequantize_fp8_kernel(const uint8_t* __restrict__ q, int64_t ld_q,
+                                                                    float a_scale, uint16_t* __restrict__ y,
+                                                                    int64_t ld_y, uint32_t units_per_row,
+                                                                    int64_t total_units) {
+  const int64_t stride = (int64_t)gridDim.x * kDq8Threads * kDq8Unroll;
+  for (int64_t g0 = (int64_t)blockIdx.x * kDq8Threads * kDq8Unroll + threadIdx.x; g0 < total_units; g0 += stride) {
+    v2u c[kDq8Unroll];
+    int64_t yo[kDq8Unroll];
+    bool ok[kDq8Unroll];
+#pragma unroll
+    for (int u = 0; u < kDq8Unroll; ++u) {
+      const int64_t g = g0 + (int64_t)u * kDq8Threads;
+      ok[u] = g < total_units;
+      const uint32_t row = ok[u] ? (uint32_t)(g / units_per_row) : 0u;
+      const uint32_t col = ok[u] ? (uint32_t)(g - (int64_t)row * units_per_row) * 8u : 0u;
+      c[u] = ok[u] ? *reinterpret_cast<const v2u*>(q + (int64_t)row * ld_q + col) : v2u{0u, 0u};
+      yo[u] = (int64_t)row * ld_y + col;
+    }
+#pragma unroll
+    for (int u = 0; u < kDq8Unroll; ++u) {
+      v4i o;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int word = (int)c[u][h];
+        const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(word, false);   // bytes 0, 1
+        const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(word, true);    // bytes 2, 3
+        o[2 * h] = (int)pack_bf16x2(lo[0] * a_scale, lo[1] * a_scale);
+        o[2 * h + 1] = (int)pack_bf16x2(hi[0] * a_scale, hi[1] * a_scale);
+      }
+      if (ok[u]) __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(y + yo[u]));
+    }
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
@@ -560,6 +605,17 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8
   const int grid = grid_for(total, kDqThreads * kDqUnroll);
   hipLaunchKernelGGL(dequantize_kernel, dim3(grid), dim3(kDqThreads), 0, stream, codes, ld_codes, scales,
                      ld_scales, y, ld_y, (uint32_t)bpr, total);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int64_t rows, int64_t cols,
+                                 uint16_t* y, int64_t ld_y, hipStream_t stream) {
+  const int64_t upr = cols / 8;
+  const int64_t total = rows * upr;
+  if (total == 0) return hipSuccess;
+  const int grid = grid_for(total, kDq8Threads * kDq8Unroll);
+  hipLaunchKernelGGL(dequantize_fp8_kernel, dim3(grid), dim3(kDq8Threads), 0, stream, q, ld_q, a_scale, y, ld_y,
+                     (uint32_t)upr, total);
   return hipGetLastError();
 }
 

@@ -6,10 +6,11 @@
 // every element of two bf16 matrices, dB = 10 log10(S / N).
 //
 // Deterministic by construction: the grid size is a function of the element count only,
-// each thread owns a fixed strided set of 8-element chunks, chunk sums are formed in
-// fp32 (a bf16 square is exact in fp32) and accumulated in fp64, workgroups reduce in a
-// fixed tree order into the workspace, and one workgroup sums the workspace in a fixed
-// order.  HBM-bound: 4 bytes read per element pair.
+// each thread owns a fixed strided set of 8-element chunks and accumulates in binary64
+// (values widened exactly; differences, squares and sums in binary64, so no intermediate
+// overflows or underflows for any finite bf16 input), workgroups
+// reduce in a fixed tree order into the workspace, and one workgroup sums the workspace
+// in a fixed order.  HBM-bound: 4 bytes read per element pair.
 #include <math.h>
 
 #include "mxq_device.hpp"
@@ -51,19 +52,21 @@ __global__ __launch_bounds__(kThreads) void sqnr_partial_kernel(const uint16_t* 
     const uint32_t col = (cc - row * chunks_per_row) * 8;
     const v4i r = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(ref + (int64_t)row * ld_ref + col));
     const v4i q = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(test + (int64_t)row * ld_test + col));
-    float cs = 0.0f, cn = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float r0 = __uint_as_float((unsigned)r[i] << 16), r1 = __uint_as_float((unsigned)r[i] & 0xFFFF0000u);
-      const float q0 = __uint_as_float((unsigned)q[i] << 16), q1 = __uint_as_float((unsigned)q[i] & 0xFFFF0000u);
-      const float d0 = r0 - q0, d1 = r1 - q1;
-      cs = fmaf(r0, r0, cs);
-      cs = fmaf(r1, r1, cs);
-      cn = fmaf(d0, d0, cn);
-      cn = fmaf(d1, d1, cn);
+      // bf16 -> binary32 -> binary64 is exact (a bf16 is the high half of a binary32);
+      // differences, squares and sums are binary64: every finite bf16 lies in
+      // [2^-133, 2^128), so no square overflows or underflows
+      const double r0 = (double)__uint_as_float((unsigned)r[i] << 16);
+      const double r1 = (double)__uint_as_float((unsigned)r[i] & 0xFFFF0000u);
+      const double q0 = (double)__uint_as_float((unsigned)q[i] << 16);
+      const double q1 = (double)__uint_as_float((unsigned)q[i] & 0xFFFF0000u);
+      const double d0 = r0 - q0, d1 = r1 - q1;
+      s = fma(r0, r0, s);
+      s = fma(r1, r1, s);
+      n = fma(d0, d0, n);
+      n = fma(d1, d1, n);
     }
-    s += (double)cs;
-    n += (double)cn;
   }
   block_reduce2(s, n, sh);
   if (threadIdx.x == 0) {

@@ -14,7 +14,8 @@ exact integer / rational arithmetic) unless the method fixes a precision:
 * ``mxfp4``    -- the MX block quantizer: 32-element blocks along K, one E8M0
   power-of-two scale per block (2^(floor(log2 amax) - 2)), E2M1 elements rounded to
   nearest with ties to even and saturated to +-6.
-* ``fp8``      -- static per-tensor FP8 E4M3 activation quantization.
+* ``fp8``      -- static per-tensor FP8 E4M3 activation quantization and its QDQ
+  dequantization to bf16.
 * ``gemm``     -- W4A4, W4A8 and bf16 reference GEMMs accumulated in float64, with the
   per-element error budget |gpu - oracle| <= 1e-5 * sum|a*b| + 1 bf16 ulp.
 * ``sqnr``     -- whole-output signal-to-quantization-noise ratio in dB.
@@ -48,7 +49,7 @@ from .formats import (  # noqa: F401
     bf16_bits_to_f64, f64_to_bf16_bits, bf16_ulp,
 )
 from .mxfp4 import block_scale_byte, quantize_mxfp4, dequantize_mxfp4, e2m1_encode  # noqa: F401
-from .fp8 import fp8_static_scales, e4m3_encode, quantize_fp8  # noqa: F401
+from .fp8 import fp8_static_scales, e4m3_encode, quantize_fp8, dequantize_fp8  # noqa: F401
 from .gemm import (  # noqa: F401
     gemm_w4a4, gemm_w4a8, gemm_bf16, within_tolerance, tolerance_bound,
 )

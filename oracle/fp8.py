@@ -12,11 +12,17 @@ Readings taken (the page gives no formula):
 * q = E4M3(fl32(x * inv_s)): one binary32 multiply (round to nearest even), then
   rounding to the nearest E4M3 value, ties to the even code, saturating magnitudes
   above 448 to 448 (no NaN is ever produced); the sign bit comes from the input.
+
+Quantize-dequantize emulation (the same section: W4A8 quality figures come from QDQ
+emulation, not from native kernels).  Reading: the dequantized activation is what a
+binary32 computation hands to a bf16 GEMM, y = bf16(fl32(e4m3(q) * s_a)) -- the exact
+E4M3 value times s_a in one binary32 multiply, then rounded to bf16 (both steps round
+to nearest even).
 """
 
 import numpy as np
 
-from .formats import E4M3_TABLE, E4M3_MAX
+from .formats import E4M3_TABLE, E4M3_MAX, e4m3_decode, f64_to_bf16_bits
 
 #: finite non-negative E4M3 magnitudes, ascending; index = code (0x00 .. 0x7E)
 _E4M3_GRID = E4M3_TABLE[:0x7F].copy()
@@ -58,3 +64,14 @@ def quantize_fp8(x, inv_s) -> np.ndarray:
         raise ValueError("quantize_fp8: non-finite input is outside the contract")
     y = x32 * np.float32(inv_s)                 # one binary32 multiply, RNE
     return e4m3_encode(y.astype(np.float64))
+
+
+def dequantize_fp8(q, s_a) -> np.ndarray:
+    """bf16 bit patterns (uint16) of bf16(fl32(e4m3(q) * s_a)) elementwise.  The NaN
+    codes S.1111.111 (never produced by quantize_fp8) give the bf16 NaN 0x7FC0 / 0xFFC0."""
+    q = np.asarray(q, dtype=np.uint8)
+    nan = (q & 0x7F) == 0x7F
+    v = e4m3_decode(np.where(nan, 0, q)).astype(np.float32)   # exact: 4 significant bits
+    y = v * np.float32(s_a)                                    # one binary32 multiply, RNE
+    bits = f64_to_bf16_bits(y.astype(np.float64))             # binary32 -> bf16, RNE
+    return np.where(nan, np.uint16(0x7FC0) | ((q >> 7).astype(np.uint16) << 15), bits).astype(np.uint16)

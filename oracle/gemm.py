@@ -34,47 +34,51 @@ from .mxfp4 import dequantize_mxfp4
 _CHUNK_ROWS = 2048
 
 
-def _chunked_product(a_rows_fn, M: int, w64: np.ndarray):
-    """out = A @ W^T and T = |A| @ |W|^T in float64, A produced chunk by chunk."""
+def _chunked_product(a_rows_fn, M: int, w64: np.ndarray, total: bool = True):
+    """out = A @ W^T and (when ``total``) T = |A| @ |W|^T in float64, A produced chunk by
+    chunk; T is None otherwise."""
     N = w64.shape[0]
     wT = w64.T
-    wTabs = np.abs(w64).T
+    wTabs = np.abs(w64).T if total else None
     out = np.empty((M, N), dtype=np.float64)
-    tot = np.empty((M, N), dtype=np.float64)
+    tot = np.empty((M, N), dtype=np.float64) if total else None
     for r0 in range(0, M, _CHUNK_ROWS):
         r1 = min(M, r0 + _CHUNK_ROWS)
         a = a_rows_fn(r0, r1)
         out[r0:r1] = a @ wT
-        tot[r0:r1] = np.abs(a) @ wTabs
+        if total:
+            tot[r0:r1] = np.abs(a) @ wTabs
     return out, tot
 
 
-def gemm_w4a4(a_codes, a_scales, w_codes, w_scales, K: int):
-    """W4A4: MXFP4 A [M,K] x MXFP4 W [N,K]^T.  Returns (out float64 [M,N], T [M,N])."""
+def gemm_w4a4(a_codes, a_scales, w_codes, w_scales, K: int, total: bool = True):
+    """W4A4: MXFP4 A [M,K] x MXFP4 W [N,K]^T.  Returns (out float64 [M,N], T [M,N] or
+    None when ``total`` is False)."""
     a_codes = np.asarray(a_codes)
     a_scales = np.asarray(a_scales)
     w64 = dequantize_mxfp4(w_codes, w_scales, K)
     M = a_codes.shape[0]
     return _chunked_product(
-        lambda r0, r1: dequantize_mxfp4(a_codes[r0:r1], a_scales[r0:r1], K), M, w64)
+        lambda r0, r1: dequantize_mxfp4(a_codes[r0:r1], a_scales[r0:r1], K), M, w64, total)
 
 
-def gemm_w4a8(a_fp8, s_a, w_codes, w_scales, K: int):
-    """W4A8: FP8 E4M3 A [M,K] (dequant scale s_a) x MXFP4 W [N,K]^T -> (out, T)."""
+def gemm_w4a8(a_fp8, s_a, w_codes, w_scales, K: int, total: bool = True):
+    """W4A8: FP8 E4M3 A [M,K] (dequant scale s_a) x MXFP4 W [N,K]^T -> (out, T or None)."""
     a_fp8 = np.asarray(a_fp8, dtype=np.uint8)
     s = float(np.float32(s_a))
     w64 = dequantize_mxfp4(w_codes, w_scales, K)
     M = a_fp8.shape[0]
-    out, tot = _chunked_product(lambda r0, r1: e4m3_decode(a_fp8[r0:r1, :K]), M, w64)
-    return out * s, tot * abs(s)
+    out, tot = _chunked_product(lambda r0, r1: e4m3_decode(a_fp8[r0:r1, :K]), M, w64, total)
+    return out * s, (tot * abs(s) if total else None)
 
 
-def gemm_bf16(a_bits, w_bits):
-    """bf16 reference: bf16 A [M,K] x bf16 W [N,K]^T over exactly widened values."""
+def gemm_bf16(a_bits, w_bits, total: bool = True):
+    """bf16 reference: bf16 A [M,K] x bf16 W [N,K]^T over exactly widened values ->
+    (out, T or None)."""
     a_bits = np.asarray(a_bits, dtype=np.uint16)
     w64 = bf16_bits_to_f64(w_bits)
     M = a_bits.shape[0]
-    return _chunked_product(lambda r0, r1: bf16_bits_to_f64(a_bits[r0:r1]), M, w64)
+    return _chunked_product(lambda r0, r1: bf16_bits_to_f64(a_bits[r0:r1]), M, w64, total)
 
 
 def to_bf16(out) -> np.ndarray:

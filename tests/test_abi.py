@@ -7,10 +7,12 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 import torch
 
 import mxfp4_microscaled_quantization_amd as mxq
+import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "mxq.h")
@@ -72,6 +74,12 @@ def _err():
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 16, 16, 16, FAKE, 8, FAKE, None), "workspace"),
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 16, 16, 16, FAKE, 1 << 20, None, None), "out3"),
     (lambda L: L.mxq_dequantize(FAKE, 16, FAKE, 1, 4, 48, FAKE, 48, None), "multiple of 32"),
+    (lambda L: L.mxq_dequantize_fp8(FAKE, 24, ctypes.c_float(1.0), 4, 24, FAKE, 24, None), "multiple of 16"),
+    (lambda L: L.mxq_dequantize_fp8(FAKE, 16, ctypes.c_float(1.0), 4, 32, FAKE, 32, None), "pitch"),
+    (lambda L: L.mxq_dequantize_fp8(FAKE, 32, ctypes.c_float(float("inf")), 4, 32, FAKE, 32, None), "finite"),
+    (lambda L: L.mxq_dequantize_fp8(FAKE_ODD, 32, ctypes.c_float(1.0), 4, 32, FAKE, 32, None), "multiples of 16"),
+    (lambda L: L.mxq_dequantize_fp8(FAKE, 32, ctypes.c_float(1.0), 4, 32, FAKE_ODD, 32, None), "16-byte"),
+    (lambda L: L.mxq_dequantize_fp8(None, 32, ctypes.c_float(1.0), 4, 32, FAKE, 32, None), "NULL"),
     (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 48, 48, FAKE, 32, FAKE, 2, 1, None), "multiple of 32"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 96, 96, 64, 0, FAKE, 48, FAKE, 3, None), "multiple of block_n"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 0, FAKE, 16, FAKE, 2, None), "ld_codes"),
@@ -136,3 +144,39 @@ def test_launch_without_gpu_reports_hip_error():
     assert "HIP error" in _err()
     with pytest.raises(mxq.MxqError):
         mxq._check(st)
+
+
+def _amax_set():
+    rng = np.random.default_rng(6)
+    return np.concatenate([rng.uniform(0.1, 1000, 300), rng.lognormal(0, 20, 300),
+                           [448.0, 1.0, 3e-5, 7e20, 3.0e38, np.finfo(np.float32).max, 1.5e-36,
+                            np.finfo(np.float32).tiny, 448.0 / np.finfo(np.float32).max * 1.0001]]).astype(np.float32)
+
+
+def test_fp8_static_scales_match_the_oracle():
+    """The library's static scales (a host computation, no GPU) equal the oracle's
+    correctly rounded quotients on the oracle's pinned amax set and wider magnitudes."""
+    for amax in _amax_set():
+        if not (448.0 / np.float64(amax) <= np.finfo(np.float32).max):
+            continue
+        s_a, inv_s = ctypes.c_float(), ctypes.c_float()
+        assert mxq.lib.mxq_fp8_static_scales(ctypes.c_float(amax), ctypes.byref(s_a), ctypes.byref(inv_s)) == 0
+        rs, ri = oracle.fp8_static_scales(amax)
+        assert np.float32(s_a.value) == rs and np.float32(inv_s.value) == ri, amax
+        assert mxq.fp8_static_scales(float(amax)) == (float(rs), float(ri))
+
+
+@pytest.mark.parametrize("amax", [0.0, -1.0, float("inf"), float("-inf"), float("nan"), 1e-40, 4e-45])
+def test_fp8_static_scales_rejects_bad_amax(amax):
+    s_a, inv_s = ctypes.c_float(-7.0), ctypes.c_float(-7.0)
+    st = mxq.lib.mxq_fp8_static_scales(ctypes.c_float(amax), ctypes.byref(s_a), ctypes.byref(inv_s))
+    assert st == mxq.MXQ_ERR_INVALID_ARG and "amax" in _err()
+    assert s_a.value == -7.0 and inv_s.value == -7.0          # outputs untouched on error
+    with pytest.raises(mxq.MxqError):
+        mxq.fp8_static_scales(amax)
+
+
+def test_fp8_static_scales_rejects_null_outputs():
+    out = ctypes.c_float()
+    assert mxq.lib.mxq_fp8_static_scales(ctypes.c_float(1.0), None, ctypes.byref(out)) == mxq.MXQ_ERR_INVALID_ARG
+    assert mxq.lib.mxq_fp8_static_scales(ctypes.c_float(1.0), ctypes.byref(out), None) == mxq.MXQ_ERR_INVALID_ARG

@@ -167,14 +167,16 @@ def _w4a8_case(mxq, a, w, label):
     return _assert_tol(to_np_bf16_bits(out), ref, tot, label)
 
 
-@pytest.mark.parametrize("M,N,K", [(300, 520, 416), (513, 257, 1024), (64, 96, 96), (1, 1, 32), (260, 300, 5120)])
-def test_w4a8_tiles_and_ragged_tails(gpu, M, N, K):
-    # i.i.d. normal activations: this case checks tiling and tails; accumulation precision
-    # under wide in-block dynamic range is covered by the workload-size and
-    # characterization tests below
-    a = workloads.activations(M, K, "normal", seed=M, name="w4a8", device="cuda")
+@pytest.mark.parametrize("dist", ["lognormal_channels", "student_t"])
+@pytest.mark.parametrize("M,N,K", [(300, 520, 416), (513, 257, 1024), (64, 96, 96), (1, 1, 32), (260, 300, 5120),
+                                   (700, 384, 288), (256, 256, 256)])
+def test_w4a8_tiles_and_ragged_tails(gpu, M, N, K, dist):
+    """Tiles and ragged tails on the W4A8 workloads' own activation models -- N(0,1) times
+    a LogNormal(0,1) per-channel scale (the Wan2.2 FFN-up) and Student-t(3) (the FFN-down)
+    -- each statically scaled from its tensor's amax, at the unchanged bar."""
+    a = workloads.activations(M, K, dist, seed=M, name="w4a8", device="cuda")
     w = workloads.weights(N, K, 0.015, seed=N, name="w4a8", device="cuda")
-    _w4a8_case(gpu, a, w, f"ragged{M}x{N}x{K}")
+    _w4a8_case(gpu, a, w, f"ragged{M}x{N}x{K}-{dist}")
 
 
 def test_w4a8_random_codes(gpu):

@@ -84,3 +84,19 @@ def test_wan_down_chain_sqnr(gpu, M):
     print(f"SQNR W4A4 gpu {d44:.4f} oracle {od44:.4f} | W4A8 gpu {d48:.4f} oracle {od48:.4f}", flush=True)
     assert abs(d44 - od44) < 0.01 and abs(d48 - od48) < 0.01
     assert d48 > d44            # FP8 activations keep more of the signal than MXFP4 ones
+
+
+def test_sqnr_extreme_magnitudes(gpu):
+    """Squares past binary32's range (|x| >= 2^64) and below its normal range (|x| <=
+    2^-64) are formed in binary64: the dB matches the oracle."""
+    rng = np.random.default_rng(44)
+    for scale in (2.0 ** 100, 2.0 ** 120, 2.0 ** -100, 2.0 ** -126):
+        ref = (rng.standard_normal((64, 256)) * scale).astype(np.float32)
+        test = (ref * (1 + 0.01 * rng.standard_normal((64, 256)))).astype(np.float32)
+        rb = oracle.f64_to_bf16_bits(ref.astype(np.float64))
+        tb = oracle.f64_to_bf16_bits(test.astype(np.float64))
+        announce(f"mxq_sqnr extreme scale 2^{math.log2(scale):.0f}")
+        s, n, d = _db(gpu.sqnr(bf16_from_bits(rb), bf16_from_bits(tb)))
+        rs, rn, rd = oracle.sqnr_db(rb, tb)
+        assert math.isfinite(d) and abs(d - rd) < 1e-6, (scale, d, rd)
+        assert abs(s - rs) <= 1e-12 * rs and abs(n - rn) <= 1e-12 * rn

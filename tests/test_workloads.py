@@ -32,3 +32,20 @@ def test_workload_table():
     for w in workloads.WORKLOADS.values():
         assert w.K % 32 == 0
     assert workloads.WORKLOADS["wan_ffn_down_sqnr"].modes == ("w4a4", "w4a8", "bf16")
+
+
+def test_host_draw_is_device_and_thread_independent(monkeypatch):
+    a1 = workloads.activations(3000, 64, "student_t", seed=5, name="thr")
+    monkeypatch.setattr(workloads, "_THREADS", 1)
+    a2 = workloads.activations(3000, 64, "student_t", seed=5, name="thr")
+    assert torch.equal(a1.view(torch.int16), a2.view(torch.int16))
+    # a reduced-M draw is the first rows of the full draw
+    a3 = workloads.activations(1500, 64, "student_t", seed=5, name="thr")
+    assert torch.equal(a3.view(torch.int16), a1[:1500].view(torch.int16))
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -1.0 - 2 ** -8 - 2 ** -20, 3.0e38], np.float32)
+    got = workloads._bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(got, ref)

@@ -4,6 +4,11 @@ This module holds only workload shapes and random-number recipes: none of the
 quantization, GEMM or SQNR arithmetic lives here, so both the CPU oracle and the HIP
 library can be fed from it without sharing any of the method's code.
 
+Every tensor is drawn on the host with NumPy, row chunk by row chunk, each chunk from its
+own stream default_rng(SeedSequence([seed, workload, tensor, chunk])), in float32, then
+rounded to bf16 (round to nearest even): a seed names the same tensor on any device and
+for any thread count.
+
 The workloads stand in for the linear layers the pages measure on (FLUX.1-dev at
 1024x768: 64x48 image tokens + 512 text tokens; batch 16; Wan2.2-14B 21x45x80 latent
 tokens).  No model weights or datasets are used.  Weights are generated directly in the
@@ -11,6 +16,10 @@ N x K (nn.Linear) layout; with i.i.d. entries this is the same distribution as t
 K x N matrix the shapes are quoted in.
 """
 
+import functools
+import os
+import warnings
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass
 from typing import Optional
 
@@ -45,19 +54,55 @@ WORKLOADS = {
 }
 
 _TENSOR_ID = {"channel_scale": 0, "act": 1, "weight": 2, "act_aux": 3}
+ROWS_PER_CHUNK = 1024          # rows drawn from one random stream
+_THREADS = max(1, min(16, len(os.sched_getaffinity(0))))
 
 
-def _seed(seed: int, name: str, tensor: str) -> int:
-    """Stable 63-bit seed per (seed, workload, tensor)."""
-    ss = np.random.SeedSequence([seed, sum(ord(c) * 131 ** i for i, c in enumerate(name)) % (2 ** 31),
-                                 _TENSOR_ID[tensor]])
-    return int(ss.generate_state(1, dtype=np.uint64)[0] & np.uint64(2 ** 63 - 1))
+def _name_id(name: str) -> int:
+    return sum(ord(c) * 131 ** i for i, c in enumerate(name)) % (2 ** 31)
 
 
-def _gen(device, seed: int, name: str, tensor: str) -> torch.Generator:
-    g = torch.Generator(device=device)
-    g.manual_seed(_seed(seed, name, tensor))
-    return g
+def _rng(seed: int, name: str, tensor: str, chunk: int) -> np.random.Generator:
+    """One host stream per (seed, workload, tensor, row chunk):
+    default_rng(SeedSequence([seed, workload id, tensor id, chunk]))."""
+    return np.random.default_rng(np.random.SeedSequence([seed, _name_id(name), _TENSOR_ID[tensor], chunk]))
+
+
+def _rows(M: int, K: int, draw) -> np.ndarray:
+    """float32 [M, K] filled chunk by chunk: rows [c*ROWS_PER_CHUNK, ...) come from
+    draw(c, rows) alone, so the result does not depend on the thread count."""
+    out = np.empty((M, K), dtype=np.float32)
+    chunks = range((M + ROWS_PER_CHUNK - 1) // ROWS_PER_CHUNK)
+
+    def fill(c):
+        r0 = c * ROWS_PER_CHUNK
+        r1 = min(M, r0 + ROWS_PER_CHUNK)
+        out[r0:r1] = draw(c, r1 - r0)
+
+    if M * K < (1 << 22) or _THREADS == 1:
+        for c in chunks:
+            fill(c)
+    else:
+        with ThreadPoolExecutor(_THREADS) as ex:
+            list(ex.map(fill, chunks))
+    return out
+
+
+def _bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even on the integer pattern (finite
+    inputs): (u + 0x7FFF + ((u >> 16) & 1)) >> 16."""
+    u = x.view(np.uint32)
+    return ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
+
+
+def _to_torch(x32: np.ndarray, device, dtype) -> torch.Tensor:
+    if dtype == torch.float32:
+        t = torch.from_numpy(x32)
+    elif dtype == torch.bfloat16:
+        t = torch.from_numpy(_bf16_bits(x32).view(np.int16)).view(torch.bfloat16)
+    else:
+        raise ValueError(f"unsupported dtype {dtype}")
+    return t.to(device) if str(device) != "cpu" else t
 
 
 def tiny_inputs(seed: int = 0):
@@ -75,60 +120,80 @@ def tiny_inputs(seed: int = 0):
     return a, np.ascontiguousarray(w_kn.T)
 
 
-def activations(M: int, K: int, kind: str, seed: int = 0, name: str = "custom",
-                device="cpu", dtype=torch.bfloat16, nu: float = 3.0) -> torch.Tensor:
-    """Activation matrix [M, K] (rows = tokens, K contiguous).
+def activations_f32(M: int, K: int, kind: str, seed: int = 0, name: str = "custom", nu: float = 3.0) -> np.ndarray:
+    """Activation matrix [M, K] as float32 on the host (rows = tokens, K contiguous).
 
     * "lognormal_channels": N(0, 1) * c_k with one c_k ~ LogNormal(0, 1) per K-channel
-      (an outlier-channel activation model).
+      (an outlier-channel activation model); c comes from its own stream.
     * "normal": i.i.d. N(0, 1).
-    * "student_t": i.i.d. Student-t with ``nu`` degrees of freedom (heavy tails),
-      drawn as Z / sqrt(G / (nu/2)) with G ~ Gamma(nu/2, 1), so 2G ~ chi^2_nu.
-    The float32 draw is rounded to ``dtype`` by torch (round to nearest even).
+    * "student_t": i.i.d. Student-t with ``nu`` degrees of freedom (heavy tails), drawn
+      as Z / sqrt(G / (nu/2)) with Z ~ N(0, 1), G ~ Gamma(nu/2, 1) (2G ~ chi^2_nu).
     """
     if kind == "normal":
-        ga = _gen(device, seed, name, "act")
-        x = torch.randn(M, K, generator=ga, device=device, dtype=torch.float32)
-    elif kind == "lognormal_channels":
-        gc = _gen(device, seed, name, "channel_scale")
-        c = torch.exp(torch.randn(K, generator=gc, device=device, dtype=torch.float32))
-        ga = _gen(device, seed, name, "act")
-        x = torch.randn(M, K, generator=ga, device=device, dtype=torch.float32)
-        x.mul_(c)
-    elif kind == "student_t":
-        ga = _gen(device, seed, name, "act")
-        x = torch.randn(M, K, generator=ga, device=device, dtype=torch.float32)
-        gg = _gen(device, seed, name, "act_aux")
-        alpha = torch.full((M, K), nu / 2.0, device=device, dtype=torch.float32)
-        g = torch._standard_gamma(alpha, generator=gg)
-        del alpha
-        g.div_(nu / 2.0).sqrt_()
-        x.div_(g)
-        del g
-    else:
-        raise ValueError(f"unknown activation kind {kind!r}")
-    return x.to(dtype) if dtype != torch.float32 else x
+        return _rows(M, K, lambda c, r: _rng(seed, name, "act", c).standard_normal((r, K), dtype=np.float32))
+    if kind == "lognormal_channels":
+        ch = np.exp(_rng(seed, name, "channel_scale", 0).standard_normal(K)).astype(np.float32)
+        return _rows(M, K, lambda c, r: _rng(seed, name, "act", c).standard_normal((r, K), dtype=np.float32) * ch)
+    if kind == "student_t":
+        half = np.float32(nu / 2.0)
+
+        def draw(c, r):
+            g = _rng(seed, name, "act_aux", c).standard_gamma(nu / 2.0, (r, K), dtype=np.float32)
+            z = _rng(seed, name, "act", c).standard_normal((r, K), dtype=np.float32)
+            return z / np.sqrt(g / half)
+
+        return _rows(M, K, draw)
+    raise ValueError(f"unknown activation kind {kind!r}")
+
+
+def activations(M: int, K: int, kind: str, seed: int = 0, name: str = "custom",
+                device="cpu", dtype=torch.bfloat16, nu: float = 3.0) -> torch.Tensor:
+    """``activations_f32`` rounded to ``dtype`` (bf16: round to nearest even) on ``device``.
+    The draw is made on the host, so a seed gives the same tensor on every device."""
+    return _to_torch(activations_f32(M, K, kind, seed, name, nu), device, dtype)
 
 
 def weights(N: int, K: int, std: float, seed: int = 0, name: str = "custom",
             device="cpu", dtype=torch.bfloat16) -> torch.Tensor:
-    """Weight matrix [N, K] ~ N(0, std), rounded to ``dtype`` by torch."""
-    g = _gen(device, seed, name, "weight")
-    w = torch.randn(N, K, generator=g, device=device, dtype=torch.float32).mul_(std)
-    return w.to(dtype) if dtype != torch.float32 else w
+    """Weight matrix [N, K] ~ N(0, std), drawn on the host, rounded to ``dtype``."""
+    s = np.float32(std)
+    w = _rows(N, K, lambda c, r: _rng(seed, name, "weight", c).standard_normal((r, K), dtype=np.float32) * s)
+    return _to_torch(w, device, dtype)
+
+
+@functools.lru_cache(maxsize=2)
+def _workload_bits(name: str, seed: int, M: int):
+    """Host bf16 bit patterns of a named workload's (A, W), kept for reuse: the full-size
+    draws take seconds and several tests and the benchmark ask for the same ones."""
+    w = WORKLOADS[name]
+    a = _bf16_bits(activations_f32(M, w.K, w.act, seed=seed, name=name))
+    s = np.float32(w.w_std)
+    wt = _bf16_bits(_rows(w.N, w.K, lambda c, r: _rng(seed, name, "weight", c).standard_normal((r, w.K),
+                                                                                            dtype=np.float32) * s))
+    a.flags.writeable = False
+    wt.flags.writeable = False
+    return a, wt
 
 
 def workload_inputs(name: str, seed: int = 0, device="cpu",
                     M: Optional[int] = None):
-    """(A, W) for a named workload as bf16 tensors on ``device``.
+    """(A, W) for a named workload as bf16 tensors on ``device`` (fresh tensors; the host
+    draw is cached).
 
-    ``M`` overrides the token count (for reduced-size parity runs of the same recipe).
+    ``M`` overrides the token count (for reduced-size parity runs of the same recipe;
+    the first M rows of the full workload's A, since rows are drawn chunk by chunk).
     """
     w = WORKLOADS[name]
     m = w.M if M is None else M
-    a = activations(m, w.K, w.act, seed=seed, name=name, device=device)
-    wt = weights(w.N, w.K, w.w_std, seed=seed, name=name, device=device)
-    return a, wt
+    a_bits, w_bits = _workload_bits(name, seed, m)
+
+    def tensor(bits):
+        with warnings.catch_warnings():      # read-only cache: the view is copied at once
+            warnings.simplefilter("ignore", UserWarning)
+            t = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16)
+        return t.clone() if str(device) == "cpu" else t.to(device)
+
+    return tensor(a_bits), tensor(w_bits)
 
 
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
