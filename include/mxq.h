@@ -235,6 +235,21 @@ mxq_status mxq_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int
                     double* out3, void* stream);
 
 /*
+ * mxq_sqnr_noalloc -- mxq_sqnr without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Same arguments, checks and results as mxq_sqnr (the same
+ * kernels, bit for bit), minus workspace / ws_bytes: the partial sums live in a 16 KB
+ * static device array of the library, one per GPU, held until the process ends; its
+ * address is looked up on the first call on each device.  Nothing is allocated or freed.
+ * Every call on one GPU shares that array, so calls that may overlap on one GPU (streams
+ * with no ordering between them) race: order them.  No state carries from one call to
+ * the next (each call writes every slot it reads).  A request needing more than the
+ * 16 KB -> MXQ_ERR_INVALID_ARG (no size does: the workspace is fixed).
+ */
+mxq_status mxq_sqnr_noalloc(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols,
+                            int64_t ld_ref, int64_t ld_test, double* out3, void* stream);
+
+/*
  * mxq_dequantize -- MXFP4 -> bf16: y = bf16(e2m1(code) * 2^(scale - 127)) (rounded to
  * nearest even only where the product leaves bf16's range: below 2^-133 or above 2^127).
  * The quantize-dequantize (QDQ) emulation step ([Q13]: W4A8 quality was measured by

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "lib", "MxqError", "quantize", "quantize_into", "quantize_hadamard", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
-    "gemm_w4a4", "gemm_w4a4_fused", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_workspace_bytes", "dequantize", "dequantize_fp8",
+    "gemm_w4a4", "gemm_w4a4_fused", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_noalloc", "sqnr_workspace_bytes", "dequantize", "dequantize_fp8",
     "mfma_ceiling", "MFMA_FLOP", "check_buffer",
     "LIB_PATH", "ABI_SYMBOLS",
 ]
@@ -47,6 +47,7 @@ ABI_SYMBOLS = {
     "mxq_gemm_bf16": (ctypes.c_int, [_ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_sqnr_workspace_bytes": (_sz, [_i64]),
     "mxq_sqnr": (ctypes.c_int, [_ptr, _ptr, _i64, _i64, _i64, _i64, _ptr, _sz, _ptr, _ptr]),
+    "mxq_sqnr_noalloc": (ctypes.c_int, [_ptr, _ptr, _i64, _i64, _i64, _i64, _ptr, _ptr]),
     "mxq_dequantize": (ctypes.c_int, [_ptr, _i64, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_dequantize_fp8": (ctypes.c_int, [_ptr, _i64, _f32, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_fp8_static_scales": (ctypes.c_int, [_f32, ctypes.POINTER(_f32), ctypes.POINTER(_f32)]),
@@ -372,6 +373,20 @@ def sqnr(ref, test, workspace=None, out3=None) -> torch.Tensor:
     check_buffer(out3, "out3", torch.float64, device=ref.device, min_numel=3)
     _check(lib.mxq_sqnr(_p(ref), _p(test), R, C, ldr, ldt, _p(workspace),
                         workspace.numel() * workspace.element_size(), _p(out3), _stream()))
+    return out3
+
+
+def sqnr_noalloc(ref, test, out3) -> torch.Tensor:
+    """Whole-output SQNR into ``out3`` (float64 [3] on ref's device) with the library's
+    own per-GPU workspace (mxq_sqnr_noalloc), for callers that cannot allocate device
+    memory.  Calls on one GPU must not overlap."""
+    _2d(ref, "ref")
+    check_buffer(ref, "ref", torch.bfloat16)
+    ldr = _rowmajor(ref, "ref")
+    R, C = ref.shape
+    ldt = check_buffer(test, "test", torch.bfloat16, (R, C), ref.device)
+    check_buffer(out3, "out3", torch.float64, device=ref.device, min_numel=3)
+    _check(lib.mxq_sqnr_noalloc(_p(ref), _p(test), R, C, ldr, ldt, _p(out3), _stream()))
     return out3
 
 

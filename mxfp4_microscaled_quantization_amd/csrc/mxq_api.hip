@@ -278,6 +278,30 @@ mxq_status mxq_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int
   return hip_status(fn, mxq::launch_sqnr(ref, test, rows, cols, ld_ref, ld_test, workspace, out3, as_stream(stream)));
 }
 
+mxq_status mxq_sqnr_noalloc(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols, int64_t ld_ref,
+                            int64_t ld_test, double* out3, void* stream) {
+  const char* fn = "mxq_sqnr_noalloc";
+  if (rows < 0 || cols < 0) return fail(MXQ_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (cols % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
+  if (ld_ref < cols || ld_test < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below cols", fn);
+  if (ld_ref % 8 != 0 || ld_test % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: pitches must be multiples of 8", fn);
+  if (rows > (int64_t)0x7FFFFFFF || cols > (int64_t)0x7FFFFFFF || rows * (cols / 8) >= ((int64_t)1 << 32))
+    return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  const size_t need = mxq::sqnr_workspace_bytes(rows * cols);
+  if (need > mxq::sqnr_scratch_bytes())
+    return fail(MXQ_ERR_INVALID_ARG, "%s: needs %zu bytes of workspace, above the library's %zu-byte scratch", fn,
+                need, mxq::sqnr_scratch_bytes());
+  if (!out3 || !aligned(out3, 8)) return fail(MXQ_ERR_INVALID_ARG, "%s: out3 must be a non-NULL 8-byte aligned pointer", fn);
+  if (rows > 0 && cols > 0) {
+    if (!ref || !test) return fail(MXQ_ERR_INVALID_ARG, "%s: ref/test is NULL", fn);
+    if (!aligned(ref, 16) || !aligned(test, 16)) return fail(MXQ_ERR_INVALID_ARG, "%s: ref/test must be 16-byte aligned", fn);
+  }
+  void* ws = nullptr;
+  hipError_t e = mxq::sqnr_scratch(&ws);
+  if (e != hipSuccess) return hip_status(fn, e);
+  return hip_status(fn, mxq::launch_sqnr(ref, test, rows, cols, ld_ref, ld_test, ws, out3, as_stream(stream)));
+}
+
 mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t* scales, int64_t ld_scales,
                           int64_t rows, int64_t cols, uint16_t* y, int64_t ld_y, void* stream) {
   const char* fn = "mxq_dequantize";

@@ -42,6 +42,10 @@ hipError_t launch_mfma_ceiling(GemmMode mode, const void* a, const uint8_t* a_sc
                                float* sink, hipStream_t stream);
 
 size_t sqnr_workspace_bytes(int64_t n);
+// The library's own SQNR workspace on the current device (a static device array,
+// sqnr_scratch_bytes() long): its device address, looked up once per device.
+size_t sqnr_scratch_bytes();
+hipError_t sqnr_scratch(void** ptr);
 hipError_t launch_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols,
                        int64_t ld_ref, int64_t ld_test, void* ws, double* out3, hipStream_t stream);
 

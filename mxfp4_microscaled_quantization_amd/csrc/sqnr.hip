@@ -13,6 +13,8 @@
 // in a fixed order.  HBM-bound: 4 bytes read per element pair.
 #include <math.h>
 
+#include <mutex>
+
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -98,9 +100,37 @@ __global__ __launch_bounds__(kThreads) void sqnr_final_kernel(const double* __re
   }
 }
 
+// The allocation-free entry point's workspace: one per GPU, in the library's own device
+// memory, held until the process ends.  Host code never passes `scratch` itself (on the
+// host it names a stand-in, not device memory); it passes the device address that
+// hipGetSymbolAddress returns for the current device.
+constexpr int kMaxDevices = 64;
+__device__ __align__(256) double scratch[2 * kMaxGroups];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
 }  // namespace
 
 size_t sqnr_workspace_bytes(int64_t) { return 2u * kMaxGroups * sizeof(double); }
+
+size_t sqnr_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t sqnr_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));   // with `dev` current
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int64_t cols, int64_t ld_ref,
                        int64_t ld_test, void* ws, double* out3, hipStream_t stream) {

@@ -73,6 +73,10 @@ def _err():
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 12, 12, 12, FAKE, 1 << 20, FAKE, None), "multiple of 8"),
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 16, 16, 16, FAKE, 8, FAKE, None), "workspace"),
     (lambda L: L.mxq_sqnr(FAKE, FAKE, 4, 16, 16, 16, FAKE, 1 << 20, None, None), "out3"),
+    (lambda L: L.mxq_sqnr_noalloc(FAKE, FAKE, 4, 12, 12, 12, FAKE, None), "multiple of 8"),
+    (lambda L: L.mxq_sqnr_noalloc(FAKE, FAKE, 4, 16, 8, 16, FAKE, None), "pitch below"),
+    (lambda L: L.mxq_sqnr_noalloc(FAKE, FAKE, 4, 16, 16, 16, None, None), "out3"),
+    (lambda L: L.mxq_sqnr_noalloc(FAKE_ODD, FAKE, 4, 16, 16, 16, FAKE, None), "16-byte"),
     (lambda L: L.mxq_dequantize(FAKE, 16, FAKE, 1, 4, 48, FAKE, 48, None), "multiple of 32"),
     (lambda L: L.mxq_dequantize_fp8(FAKE, 24, ctypes.c_float(1.0), 4, 24, FAKE, 24, None), "multiple of 16"),
     (lambda L: L.mxq_dequantize_fp8(FAKE, 16, ctypes.c_float(1.0), 4, 32, FAKE, 32, None), "pitch"),
