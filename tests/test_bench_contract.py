@@ -20,27 +20,88 @@ def test_more_than_one_gpu_is_refused():
     assert "one GPU" in r.stderr and r.stdout == ""
 
 
+class _FakeStep:
+    """The host-side fields cpu_baseline reads from a step (CPU tensors)."""
+
+    def __init__(self, modes):
+        import torch
+        import workloads
+        self.wl = workloads.GemmShape("tiny_bench", 16, 256, 64, modes, "normal", 0.02)
+        self.a = [workloads.activations(16, 256, "normal", seed=7, name="tb")]
+        self.w = workloads.weights(64, 256, 0.02, seed=7, name="tb")
+        self.s_a, self.inv_s = 0.01, 100.0
+        self.torch = torch
+
+
 def test_cpu_baseline_record():
-    rng = np.random.default_rng(7)
-    a = rng.standard_normal((16, 256)).astype(np.float32)
-    a = ((a.view(np.uint32) >> 16) << 16).view(np.float32)          # bf16-representable rows
-    w = rng.standard_normal((64, 256)).astype(np.float32) * 0.02
-    w_bits = (w.view(np.uint32) >> 16).astype(np.uint16)
-    rec = bench.cpu_baseline("tiny", 16, a, w_bits)
+    import torch
+    st = _FakeStep(("w4a4",))
+    rec = bench.cpu_baseline(None, torch, st, 16)
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["seconds"] > 0
     assert isinstance(rec["cores"], int) and rec["cores"] >= 1
-    assert "16 activation rows" in rec["sample"]
+    assert "first 16 of 16 activation rows" in rec["sample"] and "extrapolated" in rec["sample"]
+    rec8 = bench.cpu_baseline(None, torch, _FakeStep(("w4a8",)), 16)
+    assert "W4A8" in rec8["sample"] and rec8["value"] > 0
 
 
 def test_traffic_only_from_a_summary_of_the_same_source(tmp_path, monkeypatch):
+    h = bench._src_hash("gemm.hip")
     (tmp_path / "profiles").mkdir()
-    (tmp_path / "profiles" / "pmc_k_wl.txt").write_text(
+    (tmp_path / "profiles" / "pmc_mxq_gemm_w4a4_wl.txt").write_text(
+        f"kernel: k\nsource_sha256_16: {h}\nhbm_bytes_per_launch: 1.5000e+09\n")
+    (tmp_path / "profiles" / "pmc_mxq_gemm_w4a8_wl.txt").write_text(
         "kernel: k\nsource_sha256_16: 0123456789abcdef\nhbm_bytes_per_launch: 1.5000e+09\n")
+    src = tmp_path / "mxfp4_microscaled_quantization_amd" / "csrc"
+    src.mkdir(parents=True)
+    (src / "gemm.hip").write_bytes(open(os.path.join(ROOT, "mxfp4_microscaled_quantization_amd", "csrc",
+                                                     "gemm.hip"), "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
-    assert bench._traffic_from_profile("k_wl", "0123456789abcdef") == 1.5e9
-    assert bench._traffic_from_profile("k_wl", "fedcba9876543210") is None   # kernel changed since
-    assert bench._traffic_from_profile("other_wl", "0123456789abcdef") is None
+    assert bench._traffic_from_profile("mxq_gemm_w4a4", "wl") == 1.5e9
+    assert bench._traffic_from_profile("mxq_gemm_w4a8", "wl") is None    # kernel changed since
+    assert bench._traffic_from_profile("mxq_gemm_bf16", "wl") is None    # no summary
+
+
+def _write_csv(path, header, rows):
+    import csv
+    path.parent.mkdir(parents=True, exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_summary_matches_step_order(tmp_path):
+    import workloads
+    wl = workloads.WORKLOADS["wan_ffn_down_sqnr"]
+    seq = []
+    for label, n in bench.step_kernels(wl):
+        seq += [label] * n
+    names = {"mxq_gemm_bf16": "gemm_bf16_kernel", "mxq_quantize": "mx_quantize_kernel<false, false>",
+             "mxq_gemm_w4a4": "gemm_fast_kernel<0>", "mxq_quantize_fp8": "fp8_quantize_kernel<false>",
+             "mxq_gemm_w4a8": "gemm_fast_kernel<1>", "mxq_sqnr_w4a4": "sqnr_partial_kernel",
+             "mxq_sqnr_w4a8": "sqnr_partial_kernel"}
+    rows, t, did = [], 0, 0
+    for k in ["mx_quantize_kernel<false, false>", "at::native::elementwise_kernel"]:   # setup launches
+        did += 1
+        rows.append([did, f"mxq::(anonymous namespace)::{k}(int)" if "mxq" not in k and "at::" not in k else k, t, t + 5000])
+        t += 10000
+    for step in range(3):
+        for label in seq:
+            did += 1
+            dur = 1000 * (1 + seq.index(label))
+            rows.append([did, f"mxq::(anonymous namespace)::{names[label]}(mxq::Params)", t, t + dur])
+            t += dur + 10
+    _write_csv(tmp_path / "prof" / "x_kernel_trace.csv", ["Dispatch_Id", "Kernel_Name", "Start_Timestamp",
+                                                          "End_Timestamp"], rows)
+    out = tmp_path / "trace.txt"
+    sys.argv = ["bench.py", "--summarize", "trace", "--input", str(tmp_path / "prof"), "--workload",
+                "wan_ffn_down_sqnr", "--out", str(out), "--command", "rocprofv3 ... -- python bench.py --steps 2"]
+    bench.main()
+    text = out.read_text()
+    w4a4 = [ln for ln in text.splitlines() if ln.startswith("mxq_gemm_w4a4")][0]
+    assert "gemm_fast_kernel<0>" in w4a4 and " 2 " in w4a4          # the last two steps only
+    assert "command: rocprofv3" in text
 
 
 def test_committed_summaries_name_their_kernel_and_command():
