@@ -520,7 +520,7 @@ def _pmc_dispatches(d, wl, steps):
 def _copy_kib(d, counter):
     import numpy as np
     vals = [float(_col(r, "Counter_Value")) for r in _read_csvs(d, "counter_collection.csv")
-            if _col(r, "Counter_Name") == counter]
+            if _col(r, "Counter_Name") == counter and "copy" in _col(r, "Kernel_Name").lower()]
     return float(np.mean(vals))
 
 

@@ -173,3 +173,43 @@ def test_sqnr_closed_forms():
     assert math.isnan(sqnr.sqnr_db(_bf(np.zeros(3)), _bf(np.zeros(3)))[2])
     s, n, d = sqnr.sqnr_db(_bf([3.0, 4.0]), _bf([3.0, 3.0]))
     assert s == 25.0 and n == 1.0 and abs(d - 10 * math.log10(25)) < 1e-12
+
+
+def _bound_case(ref_value, T):
+    """Oracle output `ref_value` (a bf16 value) with total T; returns (out, T, ref bits, ulp)."""
+    out = np.array([[ref_value]], dtype=np.float64)
+    tot = np.array([[T]], dtype=np.float64)
+    rb = oracle.f64_to_bf16_bits(out)
+    return out, tot, rb, float(oracle.bf16_ulp(oracle.bf16_bits_to_f64(rb))[0, 0])
+
+
+@pytest.mark.parametrize("ref_value,T", [(1.0, 3000.0), (-0.0625, 400.0), (12.0, 2.5e5)])
+def test_tolerance_constant_is_1e5_at_the_boundary(ref_value, T):
+    """The bound is 1e-5 * T + 1 ulp exactly: a GPU value whose error lands just inside it
+    passes and the next bf16 value outside fails; errors between a 10x tighter and the
+    stated bound pass, errors between the stated bound and a 10x looser one fail -- so
+    both a 1e-6 and a 1e-4 constant would break this test."""
+    out, tot, rb, ulp = _bound_case(ref_value, T)
+    bound = 1e-5 * T + ulp
+    ref = float(oracle.bf16_bits_to_f64(rb)[0, 0])
+    # bf16 values on the grid above ref: the last one within the bound, the first outside
+    vals = ref + ulp * np.arange(0, 4 * int(bound / ulp) + 8)
+    bits = oracle.f64_to_bf16_bits(vals)
+    back = oracle.bf16_bits_to_f64(bits)
+    inside = back[np.abs(back - ref) <= bound].max()
+    outside = back[np.abs(back - ref) > bound].min()
+    for v, expect in ((inside, True), (outside, False)):
+        ok, err, b = oracle.within_tolerance(oracle.f64_to_bf16_bits(np.array([[v]])), out, tot)
+        assert bool(ok[0, 0]) is expect and abs(b[0, 0] - bound) <= 1e-12 * bound, (v, expect, err, b)
+    # between 1e-6 T + ulp and 1e-5 T + ulp: accepted; between 1e-5 T + ulp and 1e-4 T + ulp: rejected
+    mid_lo = ref + 0.5 * (1e-6 * T + 1e-5 * T) + ulp
+    mid_hi = ref + 0.5 * (1e-5 * T + 1e-4 * T) + ulp
+    for v, expect in ((mid_lo, True), (mid_hi, False)):
+        vb = oracle.f64_to_bf16_bits(np.array([[v]]))
+        err = abs(float(oracle.bf16_bits_to_f64(vb)[0, 0]) - ref)
+        if expect:
+            assert err <= bound
+        else:
+            assert err > bound and err <= 1e-4 * T + 2 * ulp
+        ok, _, _ = oracle.within_tolerance(vb, out, tot)
+        assert bool(ok[0, 0]) is expect

@@ -81,3 +81,30 @@ def test_rotation_rejects_bad_sizes():
         rotate_f32(np.zeros((1, 40), np.float32), 16)
     with pytest.raises(ValueError):
         hadamard_matrix(12)
+
+
+@pytest.mark.parametrize("n", [16, 64, 256])
+def test_binary32_butterfly_codes_against_the_exact_rotation(n):
+    """How far the binary32 butterfly (the rotation both sides compute) moves the MXFP4
+    codes from those of the exact x H / sqrt(n) (float64 products and sums, exact here:
+    bf16 inputs spanning < 40 binades plus 8 bits of growth fit 53 bits).  Codes may
+    differ only where the exact value sits within binary32 rounding of a rounding
+    boundary: then by one step of the E2M1 grid, and rarely."""
+    import workloads
+    u = workloads.activations_f32(256, 4096, "student_t", seed=n, name="hd-exact").view(np.uint32)
+    x = (((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)) << np.uint32(16)).view(np.float32)
+    h = oracle.hadamard_matrix(n).astype(np.float64)
+    exact = (x.astype(np.float64).reshape(-1, n) @ h / np.sqrt(n)).reshape(x.shape)
+    c_exact, s_exact = oracle.quantize_mxfp4(exact)
+    c_b32, s_b32 = oracle.quantize_mxfp4_rotated(x, n)
+    assert np.mean(s_exact != s_b32) < 1e-3
+    same_scale = np.repeat(s_exact == s_b32, 16, axis=1)
+    unpack = lambda c: np.stack([c & 0xF, c >> 4], axis=-1).reshape(c.shape[0], -1)   # noqa: E731
+    ue, ub = unpack(c_exact), unpack(c_b32)
+    mag = lambda c: (c & 7).astype(int)   # noqa: E731
+    diff = (ue != ub) & np.repeat(s_exact == s_b32, 32, axis=1)
+    frac = diff.mean()
+    print(f"n={n}: {int(diff.sum())} of {diff.size} codes differ from the exact rotation ({frac:.2e})")
+    assert frac < 1e-3
+    assert np.all(np.abs(mag(ue[diff]) - mag(ub[diff])) <= 1)
+    assert same_scale.shape[1] * 2 == ue.shape[1]
