@@ -33,6 +33,7 @@
 //    MFMA throughput on real data than 32 x 32 x 16.
 //  * gemm_w4a4_fused8_kernel takes unquantized activations and quantizes each activation
 //    tile into LDS inside the GEMM, bit-identically to the separate quantizer.
+#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -91,6 +92,20 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+
+// The lane index, re-derived where it is called: the asm statement cannot be moved, so
+// address arithmetic built on it stays where it is used (a persistent kernel's epilogue
+// addresses would otherwise be hoisted out of the tile loop and held across the K loop).
+__device__ __forceinline__ uint32_t lane_here() {
+  uint32_t l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Column of byte `col` (0..31) of a row of a 32-byte-per-row scale chunk in LDS, for a row
+// whose index within its 32-row line is r: rows with bit 2 set hold their 16-byte halves
+// swapped (the chunk loads place them so).
+__device__ __forceinline__ uint32_t sc_col(uint32_t col, uint32_t r) { return col ^ (16u * ((r >> 2) & 1u)); }
 
 struct Params {
   const uint8_t* a;
@@ -444,6 +459,57 @@ __device__ __forceinline__ void mfma16(v16f (&acc)[4][4], const v4i (&f)[12], co
     }
 }
 
+// Epilogue of tiles the staged path does not take (a partial column tile or an output
+// that is not 16-byte aligned): a lane owns 4 consecutive columns per store.
+template <int MODE>
+__device__ __forceinline__ void store_partial_tile(const Params& p, const v16f (&acc)[4][4], uint32_t lane, uint32_t wm,
+                                                   uint32_t wn, int m0, int n0) {
+  const uint32_t r32 = lane & 31, g = lane >> 5;
+  const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = m0 + (int)(wm * 128 + 32 * j + r32);
+    uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+#pragma unroll
+      for (int pp = 0; pp < 4; ++pp) {
+        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
+        float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+        float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+        if constexpr (MODE == GEMM_W4A8) {
+          v0 *= p.a_scale;
+          v1 *= p.a_scale;
+          v2 *= p.a_scale;
+          v3 *= p.a_scale;
+        }
+        const unsigned lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
+        if (full) {
+          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+        } else if (m < p.M) {
+          if (p.vec_store && n + 4 <= p.N) {
+            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
+          } else {
+            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
+            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
+            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
+            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
+          }
+        }
+      }
+    }
+  }
+}
+
+// Whether gemm_fast_kernel<MODE> runs persistent workgroups (a grid of at most one
+// workgroup per compute unit, each looping over tiles).  W4A4 gains from overlapping each
+// tile's epilogue and the next tile's first loads (3-4 % on the FLUX and Wan shapes); in
+// the W4A8 build the loop's live state pushes per-tile spill reloads onto memory waits
+// and it loses 4-6 %, so W4A8 launches one workgroup per tile (the loop then runs once
+// and the next-tile code folds away).
+template <int MODE>
+constexpr bool kPersistent = MODE == GEMM_W4A4;
+
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   using C = Fast<MODE>;
@@ -475,26 +541,41 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
   const uint32_t wm = wave & 1, wn = wave >> 1;
 
+  // Persistent workgroups: workgroup b runs tiles b, b + G, b + 2G, ... (G = gridDim.x, a
+  // multiple of 8 whenever it is below the tile count).  The hardware places workgroup b
+  // on XCD b mod 8, and so is every tile it runs; the XCD-aware raster below hands the
+  // workgroups of one XCD consecutive runs of the grouped tile order, round after round.
   const int nt = p.tiles_m * p.tiles_n;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, local = bid >> 3;
   const int q8 = nt >> 3, r8 = nt & 7;
-  const int seq = xcd * q8 + min(xcd, r8) + local;
-  const int group = seq / (GROUP_M * p.tiles_n);
-  const int first_m = group * GROUP_M;
-  const int gm = min(GROUP_M, p.tiles_m - first_m);
-  const int in_group = seq - group * GROUP_M * p.tiles_n;
-  const int tm = first_m + in_group % gm, tn = in_group / gm;
-  const int m0 = tm * BM, n0 = tn * BN;
-
-  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
-  const bool has_ws = MODE != GEMM_BF16, has_as = MODE == GEMM_W4A4;
-  const __amdgpu_buffer_rsrc_t rsw =
-      make_rsrc(has_ws ? p.w_scales + (int64_t)n0 * p.scale_row_bytes : p.w, has_ws ? rows_w * p.scale_row_bytes : 0);
-  const __amdgpu_buffer_rsrc_t rsa =
-      make_rsrc(has_as ? p.a_scales + (int64_t)m0 * p.scale_row_bytes : p.a, has_as ? rows_a * p.scale_row_bytes : 0);
+  auto tile_origin_of = [&](int t, int& m0_, int& n0_) {
+    const int xcd = t & 7, local = t >> 3;
+    const int seq = xcd * q8 + min(xcd, r8) + local;
+    const int group = seq / (GROUP_M * p.tiles_n);
+    const int first_m = group * GROUP_M;
+    const int gm = min(GROUP_M, p.tiles_m - first_m);
+    const int in_group = seq - group * GROUP_M * p.tiles_n;
+    m0_ = (first_m + in_group % gm) * BM;
+    n0_ = (in_group / gm) * BN;
+  };
+  constexpr bool has_as = MODE == GEMM_W4A4;
+  // buffer resources of one tile: activation rows, weight rows and their scale rows
+  struct TileRes {
+    __amdgpu_buffer_rsrc_t a, w, sw, sa;
+  };
+  auto tile_res = [&](int m0_, int n0_) {
+    const uint32_t rows_a = (uint32_t)min(BM, p.M - m0_), rows_w = (uint32_t)min(BN, p.N - n0_);
+    TileRes r;
+    r.a = make_rsrc(p.a + (int64_t)m0_ * p.a_row_bytes, rows_a * p.a_row_bytes);
+    r.w = make_rsrc(p.w + (int64_t)n0_ * p.w_row_bytes, rows_w * p.w_row_bytes);
+    r.sw = make_rsrc(p.w_scales + (int64_t)n0_ * p.scale_row_bytes, rows_w * p.scale_row_bytes);
+    r.sa = make_rsrc(has_as ? p.a_scales + (int64_t)m0_ * p.scale_row_bytes : p.a,
+                     has_as ? rows_a * p.scale_row_bytes : 0);
+    return r;
+  };
+  int t = blockIdx.x;
+  int m0, n0;
+  tile_origin_of(t, m0, n0);
+  TileRes cur = tile_res(m0, n0);
 
   // Lane geometry of the direct-to-LDS tile loads: LDS line q holds rows
   // [q * ROWS_PER_LINE, ...); lane i lands at byte 16 i of the line, i.e. in row i / CPR at
@@ -514,45 +595,82 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   uint32_t a_voff0, a_voff1, w_voff0, w_voff1;
   dma_voffs(A_CPR, p.a_row_bytes, a_voff0, a_voff1);
   dma_voffs(W_CPR, p.w_row_bytes, w_voff0, w_voff1);
-  // scale chunk lines: lane i fetches bytes 16 (i & 1) .. + 16 of row i / 2 of the line
-  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
+  // scale chunk lines: lane i lands in half i & 1 of row i / 2 of the line; rows with bit 2
+  // set hold their two 16-byte halves swapped (sc_col), which halves the bank conflicts of
+  // the 4-byte scale reads (32 lanes on 32 rows 32 bytes apart)
+  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (((lane & 1) ^ ((lane >> 3) & 1)) * 16);
 
   // A window's tile loads in two parts, issued under different MFMA steps so that the
   // four waves never queue a whole window of DMA at once: part 0 = activation tile,
   // part 1 = weight tile.
-  // ring slots of window w's tiles
-  auto a_slot = [&](int w) { return lds + (uint32_t)(w % NS) * A_TILE; };
-  auto w_slot = [&](int w) { return lds + W_BASE + (uint32_t)(w % NS) * W_TILE; };
-  // one line of window w's tile: part 0 = activation tile, part 1 = weight tile
-  auto issue_line = [&](int w, auto part_tag, int j) {
+  // Ring slots: window w of the current tile lives in tile slot (wb + w) mod NS, its scale
+  // chunk c in scale slot (cb + c) & 1; wb and cb advance by the tile's window and chunk
+  // counts from tile to tile, so the next tile's first windows fill the slots the current
+  // tile's last windows leave free.
+  uint32_t wb = 0, cb = 0;
+  auto a_slot = [&](int w) { return lds + ((wb + (uint32_t)w) % NS) * A_TILE; };
+  auto w_slot = [&](int w) { return lds + W_BASE + ((wb + (uint32_t)w) % NS) * W_TILE; };
+  // one line of window w's tile of tile `r` (ring slot of window w of the current tile
+  // numbering): part 0 = activation tile, part 1 = weight tile
+  // lane offsets of the tile loads: {a even, a odd, w even, w odd}
+  struct DmaOffs {
+    uint32_t a0, a1, w0, w1;
+  };
+  const DmaOffs voffs{a_voff0, a_voff1, w_voff0, w_voff1};
+  // the same offsets computed afresh, for the once-per-tile loads (the long-lived copies
+  // may sit in scratch there, and a reload would wait for every load in flight)
+  auto fresh_voffs = [&]() {
+    const uint32_t l = lane_here();
+    auto one = [&](uint32_t cpr, uint32_t row_bytes, uint32_t& even, uint32_t& odd) {
+      const uint32_t row = l / cpr, slot = l % cpr;
+      if (cpr == 8) {
+        even = row * row_bytes + ((slot ^ ((row >> 1) & 7u)) * 16);
+        odd = row * row_bytes + ((slot ^ (((8u + row) >> 1) & 7u)) * 16);
+      } else {
+        even = odd = row * row_bytes + ((slot ^ ((row >> 2) & 3u)) * 16);
+      }
+    };
+    DmaOffs d;
+    one(A_CPR, p.a_row_bytes, d.a0, d.a1);
+    one(W_CPR, p.w_row_bytes, d.w0, d.w1);
+    return d;
+  };
+  auto issue_line_of = [&](const TileRes& r, const DmaOffs& vo, int slot_w, int w, auto part_tag, int j) {
     constexpr int PART = decltype(part_tag)::value;
     if constexpr (PART == 0) {
       const uint32_t line = wave * A_LINES + j;
-      load_line_to_lds(ra, a_slot(w) + line * 1024, (line & 1) ? a_voff1 : a_voff0,
+      load_line_to_lds(r.a, a_slot(slot_w) + line * 1024, (line & 1) ? vo.a1 : vo.a0,
                        (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
     } else {
       const uint32_t line = wave * W_LINES + j;
-      load_line_to_lds(rw, w_slot(w) + line * 1024, (line & 1) ? w_voff1 : w_voff0,
+      load_line_to_lds(r.w, w_slot(slot_w) + line * 1024, (line & 1) ? vo.w1 : vo.w0,
                        (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
     }
   };
-  auto issue_loads = [&](int w) {
+  auto issue_line = [&](int w, auto part_tag, int j) { issue_line_of(cur, voffs, w, w, part_tag, j); };
+  auto issue_loads_with = [&](const DmaOffs& vo, int w) {
 #pragma unroll
-    for (int j = 0; j < A_LINES; ++j) issue_line(w, std::integral_constant<int, 0>{}, j);
+    for (int j = 0; j < A_LINES; ++j) issue_line_of(cur, vo, w, w, std::integral_constant<int, 0>{}, j);
 #pragma unroll
-    for (int j = 0; j < W_LINES; ++j) issue_line(w, std::integral_constant<int, 1>{}, j);
+    for (int j = 0; j < W_LINES; ++j) issue_line_of(cur, vo, w, w, std::integral_constant<int, 1>{}, j);
   };
-  // scale chunk c (windows c*CW ..) into slot c & 1
+  auto issue_loads = [&](int w) { issue_loads_with(voffs, w); };
+  // scale chunk c (windows c*CW ..) of tile `r` into scale slot (cb + slot_c) & 1
   const int nchunks = (p.nwin + CW - 1) / CW;
-  auto issue_chunk = [&](int c) {
-    uint8_t* slot = lds + SC_BASE + (uint32_t)(c & 1) * SLOT;
+  auto issue_chunk_of = [&](const TileRes& r, uint32_t sc_vo, int slot_c, int c) {
+    uint8_t* slot = lds + SC_BASE + ((cb + (uint32_t)slot_c) & 1u) * SLOT;
 #pragma unroll
     for (int j = 0; j < SC_LINES; ++j) {
       const uint32_t line = wave * SC_LINES + j;
       const bool is_w = line < BN / 32;
       const uint32_t row0 = (is_w ? line : line - BN / 32) * 32;
-      load_line_to_lds(is_w ? rsw : rsa, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
+      load_line_to_lds(is_w ? r.sw : r.sa, slot + line * 1024, sc_vo, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
     }
+  };
+  auto issue_chunk = [&](int c) { issue_chunk_of(cur, sc_voff, c, c); };
+  auto fresh_sc_voff = [&]() {
+    const uint32_t l = lane_here();
+    return (l >> 1) * p.scale_row_bytes + (((l & 1) ^ ((l >> 3) & 1)) * 16);
   };
   // Chunk c+1 goes out at the start of window c*CW (c >= 1; chunk 1 in the prologue): the
   // barrier that ended window c*CW - 1 follows every wave's last read of chunk c-1, the
@@ -560,33 +678,28 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // the chunk older than every tile load the hand-over waits for.
   auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
   // this lane's scale bytes for window w: W rows (4 n-fragments), A rows (4 m-fragments);
-  // byte t is the block of MFMA step t (op_sel t)
+  // byte t is the block of MFMA step t (op_sel t).  sc_lane: the lane's row (lane & 31)
+  // within a 32-row line, its group's 4-byte column (W4A4) and the half swap of sc_col.
+  const uint32_t sc_lane = (lane & 31u) * SC_ROW | ((SC_WIN == 8) ? 4u * (lane >> 5) : 0u) | (16u * ((lane >> 2) & 1u));
   auto read_scales = [&](int w, uint32_t (&scw)[4], uint32_t (&sca)[4]) {
     if constexpr (HAS_SC) {
-      // lane group g's blocks g*STEPS .. g*STEPS+STEPS-1 as bytes 0.. of one word
-      const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
-      const uint32_t g = lane >> 5, r32 = lane & 31;
-      const uint32_t col = (uint32_t)(w % CW) * SC_WIN + ((SC_WIN == 8) ? 4 * g : 0);
-      const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * g;
+      // lane group g's blocks g*STEPS .. g*STEPS+STEPS-1 as bytes 0.. of one word; the
+      // window's column (bits 2-4 of the row offset) enters as one XOR with sc_lane
+      const uint8_t* slot = lds + SC_BASE + ((cb + (uint32_t)(w / CW)) & 1u) * SLOT;
+      const uint32_t off = sc_lane ^ ((uint32_t)(w % CW) * SC_WIN);
+      const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * (lane >> 5);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        scw[i] = *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i + r32) * SC_ROW + col) >> sh;
+        scw[i] = *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i) * SC_ROW + off) >> sh;
       if constexpr (MODE == GEMM_W4A4) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-          sca[j] = *reinterpret_cast<const uint32_t*>(slot + (BN + wm * 128 + 32 * j + r32) * SC_ROW + col) >> sh;
+          sca[j] = *reinterpret_cast<const uint32_t*>(slot + (BN + wm * 128 + 32 * j) * SC_ROW + off) >> sh;
       }
     }
   };
 
   v16f acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
   const int nwin = p.nwin;
   uint32_t scw[4] = {0, 0, 0, 0}, sca[4] = {0, 0, 0, 0};
   v4i f0[12], f1[12];
@@ -620,13 +733,39 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // region.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  auto window = [&](int w, auto pend_tag, auto steady_tag) {
+  TileRes nxt = cur;
+  bool has_next = false;
+  int t_next = 0;
+  auto window = [&](int w, auto pend_tag, auto steady_tag, auto next_tag) {
     constexpr bool PEND = decltype(pend_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
+    constexpr bool NEXT = decltype(next_tag)::value;
     const uint8_t* la = a_slot(w);
     const uint8_t* lw = w_slot(w);
     if constexpr (HAS_SC)
       if (chunk_due(w)) issue_chunk(w / CW + 1);
+    if constexpr (NEXT) {
+      // Last window: the next tile's windows 0 .. NS-2 go to the slots after this one (free
+      // since the hand-overs of windows nwin-NS .. nwin-2) and its scale chunk 0 to the
+      // scale slot after this tile's last chunk (free since that chunk's predecessor was
+      // last read).  Each is older than the hand-over's full wait below.
+      if (has_next) {
+        int m0n, n0n;
+        tile_origin_of(t_next, m0n, n0n);
+        nxt = tile_res(m0n, n0n);
+        if constexpr (HAS_SC) issue_chunk_of(nxt, fresh_sc_voff(), nchunks, 0);
+        const DmaOffs fo = fresh_voffs();
+#pragma unroll
+        for (int k = 0; k + 1 < NS; ++k) {
+          if (k < nwin) {
+#pragma unroll
+            for (int j = 0; j < A_LINES; ++j) issue_line_of(nxt, fo, nwin + k, k, I0{}, j);
+#pragma unroll
+            for (int j = 0; j < W_LINES; ++j) issue_line_of(nxt, fo, nwin + k, k, I1{}, j);
+          }
+        }
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
     // step-0 tile loads, spread over the reads of step 0
     auto pend_loads = [&](int k) {
@@ -715,89 +854,82 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  int w = 0;
-  if (nwin > NS) {
-    window(0, F_{}, T_{});
-    for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{});
-    window(w, T_{}, F_{});
-    ++w;
-  }
-  for (; w < nwin; ++w) window(w, F_{}, F_{});
+  for (;;) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    t_next = t + (int)gridDim.x;
+    has_next = kPersistent<MODE> && t_next < nt;
+    int w = 0;
+    if (nwin > NS) {
+      window(0, F_{}, T_{}, F_{});
+      for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{}, F_{});
+      window(w, T_{}, F_{}, F_{});
+      ++w;
+    }
+    for (; w < nwin - 1; ++w) window(w, F_{}, F_{}, F_{});
+    window(nwin - 1, F_{}, F_{}, T_{});
 
-  // ---- epilogue: fp32 -> bf16 (RNE) ----
-  const uint32_t r32 = lane & 31, g = lane >> 5;
-  if (p.vec16 && n0 + BN <= p.N) {
-    // A lane holds 4 consecutive columns of 32 different rows, so a direct store touches
-    // 32 cache lines per instruction.  Each wave instead parks its 128 x 128 sub-tile in
-    // its own 32 KB of LDS (16-byte chunk c of row r at slot c ^ (r & 15), spreading the
-    // writes of 16 rows over all banks) and stores 4 whole 256-byte row segments per
-    // instruction.  After the last hand-over barrier no wave reads tile data from LDS.
-    __syncthreads();
-    uint8_t* sub = lds + wave * (128u * 256u);
+    // ---- epilogue: fp32 -> bf16 (RNE) ----
+    const uint32_t el = lane_here();
+    if (p.vec16 && n0 + BN <= p.N) {
+      // A lane holds 4 consecutive columns of 32 different rows, so a direct store touches
+      // 32 cache lines per instruction.  Each wave instead parks 32 rows of its 128 x 128
+      // sub-tile at a time in its own 8 KB of the last window's activation slot (free after
+      // the last hand-over barrier; 16-byte chunk c of row r at slot c ^ (r & 15), spreading
+      // the writes of 16 rows over all banks) and stores 4 whole 256-byte row segments per
+      // instruction.  The stores drain under the next tile's first window.
+      uint8_t* sub = a_slot(nwin - 1) + wave * (32u * 256u);
+      const int mw = m0 + (int)wm * 128;
+      uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t row = 32 * j + r32;
+      for (int j = 0; j < 4; ++j) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int pp = 0; pp < 4; ++pp) {
-          float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
-          float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
-          if constexpr (MODE == GEMM_W4A8) {
-            v0 *= p.a_scale;
-            v1 *= p.a_scale;
-            v2 *= p.a_scale;
-            v3 *= p.a_scale;
+          for (int pp = 0; pp < 4; ++pp) {
+            float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
+            float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
+            if constexpr (MODE == GEMM_W4A8) {
+              v0 *= p.a_scale;
+              v1 *= p.a_scale;
+              v2 *= p.a_scale;
+              v3 *= p.a_scale;
+            }
+            const uint32_t chunk = 4 * i + pp, er = el & 31;
+            *reinterpret_cast<v2u*>(sub + er * 256 + ((chunk ^ (er & 15)) << 4) + 8 * (el >> 5)) =
+                v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
+            if (pp == 3) __builtin_amdgcn_sched_barrier(0);
           }
-          const uint32_t chunk = 4 * i + pp;
-          *reinterpret_cast<v2u*>(sub + row * 256 + ((chunk ^ (row & 15)) << 4) + 8 * g) =
-              v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
-        }
-    }
-    const int mw = m0 + (int)wm * 128;
-    uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-      const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
-      const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
-      if (mw + (int)row < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)row * p.ld_out + c * 8) = v;
-    }
-    return;
-  }
-  // partial column tiles: a lane owns 4 consecutive columns per store
-  const bool full = p.vec_store && m0 + BM <= p.M && n0 + BN <= p.N;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int m = m0 + (int)(wm * 128 + 32 * j + r32);
-    uint16_t* orow = p.out + (int64_t)min(m, p.M - 1) * p.ld_out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-      for (int pp = 0; pp < 4; ++pp) {
-        const int n = n0 + (int)(wn * 128 + 32 * i + 8 * pp + 4 * g);
-        float v0 = acc[i][j][4 * pp + 0], v1 = acc[i][j][4 * pp + 1];
-        float v2 = acc[i][j][4 * pp + 2], v3 = acc[i][j][4 * pp + 3];
-        if constexpr (MODE == GEMM_W4A8) {
-          v0 *= p.a_scale;
-          v1 *= p.a_scale;
-          v2 *= p.a_scale;
-          v3 *= p.a_scale;
-        }
-        const unsigned lo = pack_bf16x2(v0, v1), hi = pack_bf16x2(v2, v3);
-        if (full) {
-          *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
-        } else if (m < p.M) {
-          if (p.vec_store && n + 4 <= p.N) {
-            *reinterpret_cast<v2u*>(orow + n) = v2u{lo, hi};
-          } else {
-            if (n + 0 < p.N) orow[n + 0] = (uint16_t)lo;
-            if (n + 1 < p.N) orow[n + 1] = (uint16_t)(lo >> 16);
-            if (n + 2 < p.N) orow[n + 2] = (uint16_t)hi;
-            if (n + 3 < p.N) orow[n + 3] = (uint16_t)(hi >> 16);
-          }
+        for (int q = 0; q < 8; ++q) {
+          const uint32_t row = 4 * q + (el >> 4), c = el & 15;
+          const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
+          const int orow = 32 * j + (int)row;
+          if (mw + orow < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)orow * p.ld_out + c * 8) = v;
         }
       }
+    } else {
+      store_partial_tile<MODE>(p, acc, el, wm, wn, m0, n0);
     }
+    if (!has_next) break;
+    // Next tile: its window 0 and scale chunk 0 are resident (the last hand-over waited for
+    // them); once every wave has read its staged rows back, window NS-1 may refill the last
+    // window's slot and chunk 1 the last chunk's scale slot.
+    stage_barrier();
+    wb = (wb + (uint32_t)nwin) % NS;
+    cb = (cb + (uint32_t)nchunks) & 1u;
+    t = t_next;
+    tile_origin_of(t, m0, n0);
+    cur = nxt;
+    if constexpr (HAS_SC)
+      if (nchunks > 1) issue_chunk_of(cur, fresh_sc_voff(), 1, 1);
+    if (NS - 1 < nwin) issue_loads_with(fresh_voffs(), NS - 1);
+    read_frags<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
+    read_scales(0, scw, sca);
   }
 }
 
@@ -1376,7 +1508,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_w4a4_fused8_kernel(Params p) {
   const uint32_t wr = lane >> 3, wsl = lane & 7;
   const uint32_t w_voff0 = wr * p.w_row_bytes + ((wsl ^ ((wr >> 1) & 7u)) * 16);
   const uint32_t w_voff1 = wr * p.w_row_bytes + ((wsl ^ (((8u + wr) >> 1) & 7u)) * 16);
-  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (lane & 1) * 16;
+  const uint32_t sc_voff = (lane >> 1) * p.scale_row_bytes + (((lane & 1) ^ ((lane >> 3) & 1)) * 16);
   // load i of quarter q covers rows 32v + 8q + 2i + (lane / 32), elements 8 (lane % 32) ..
   // of the window; the code slot of row r, block b is b ^ ((r >> 1) & 7) = b ^ (4 (q & 1) + i)
   const uint32_t h = lane >> 5, b = (lane & 31) >> 2, k = lane & 3;
@@ -1402,7 +1534,7 @@ __global__ __launch_bounds__(NT8, 1) void gemm_w4a4_fused8_kernel(Params p) {
   auto chunk_due = [&](int w) { return w >= CW && w % CW == 0 && w / CW + 1 < nchunks; };
   auto read_w_scale = [&](int w, uint32_t ln, int i) {
     const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
-    const uint32_t col = (uint32_t)(w % CW) * 8 + 4 * (ln >> 5);
+    const uint32_t col = sc_col((uint32_t)(w % CW) * 8 + 4 * (ln >> 5), ln & 31);
     return *reinterpret_cast<const uint32_t*>(slot + (wn * 128 + 32 * i + (ln & 31)) * SC_ROW + col);
   };
   auto read_a_scale = [&](int par, uint32_t ln, int j) {
@@ -1632,6 +1764,20 @@ __global__ __launch_bounds__(NT8, 1) void gemm_w4a4_fused8_kernel(Params p) {
   }
 }
 
+// Compute units of the current device (the persistent kernels' grid), read once per device.
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,
@@ -1668,10 +1814,16 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
       // the bf16 reference runs its 16 x 16 eight-wave kernel; the scaled modes the
       // four-wave 32 x 32 kernel, whose W4A4 MFMA order the fused kernel reproduces bit
       // for bit (eight waves of 32 x 32 MFMAs measured slower for both scaled modes)
-      if constexpr (MD == GEMM_BF16)
+      if constexpr (MD == GEMM_BF16) {
         hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(NT16), 0, stream, p);
-      else
-        hipLaunchKernelGGL(gemm_fast_kernel<MD>, grid, block, 0, stream, p);
+      } else {
+        // one persistent workgroup per compute unit (a multiple of 8, so every tile of a
+        // workgroup maps to its XCD), or one per tile when there are fewer tiles
+        const int cus = kPersistent<MD> ? device_cu_count() & ~7 : 0;
+        const int nt = p.tiles_m * p.tiles_n;
+        const dim3 pgrid((unsigned)(cus > 0 && cus < nt ? cus : nt));
+        hipLaunchKernelGGL(gemm_fast_kernel<MD>, pgrid, block, 0, stream, p);
+      }
     } else {
       p.nwin = (int)((K + Cfg<MD>::K_WIN - 1) / Cfg<MD>::K_WIN);
       hipLaunchKernelGGL(gemm_generic_kernel<MD>, grid, block, 0, stream, p);
