@@ -19,7 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxq.so")
 ARCH = "gfx950"
 
-SOURCES = ["mxq_api.hip", "quantize.hip", "gemm.hip", "sqnr.hip", "ceiling.hip"]
+SOURCES = ["mxq_api.hip", "quantize.hip", "gemm.hip", "gemm_w4a8.hip", "sqnr.hip", "ceiling.hip"]
+# per-source compiler options (gemm_w4a8.hip: see the comment at its top)
+SOURCE_FLAGS = {"gemm_w4a8.hip": ["-mllvm", "-disable-machine-sink"]}
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
@@ -51,7 +53,7 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
     def compile_one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [hipcc(), *compile_flags, *extra_flags, "-c", "-o", obj, os.path.join(CSRC, src)]
+        cmd = [hipcc(), *compile_flags, *SOURCE_FLAGS.get(src, []), *extra_flags, "-c", "-o", obj, os.path.join(CSRC, src)]
         if verbose:
             print(" ".join(cmd), flush=True)
         res = subprocess.run(cmd, capture_output=True, text=True)

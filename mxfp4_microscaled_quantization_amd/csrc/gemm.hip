@@ -107,6 +107,10 @@ __device__ __forceinline__ uint32_t lane_here() {
 // swapped (the chunk loads place them so).
 __device__ __forceinline__ uint32_t sc_col(uint32_t col, uint32_t r) { return col ^ (16u * ((r >> 2) & 1u)); }
 
+}  // namespace
+
+// Kernel arguments of every GEMM kernel here (named, so that the W4A8 object built from
+// this file with MXQ_GEMM_W4A8_OBJECT shares the type with its launcher).
 struct Params {
   const uint8_t* a;
   const uint8_t* a_scales;
@@ -122,6 +126,8 @@ struct Params {
   int vec16;       // 16-byte output stores allowed
   int scale_dword_ok;
 };
+
+namespace {
 
 // LDS swizzles.  The LDS serves a ds_read_b128 16 lanes at a time over 64 4-byte banks
 // (256 bytes); fragment reads have 16 consecutive lanes on 16 consecutive rows at one
@@ -608,8 +614,11 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // counts from tile to tile, so the next tile's first windows fill the slots the current
   // tile's last windows leave free.
   uint32_t wb = 0, cb = 0;
-  auto a_slot = [&](int w) { return lds + ((wb + (uint32_t)w) % NS) * A_TILE; };
-  auto w_slot = [&](int w) { return lds + W_BASE + ((wb + (uint32_t)w) % NS) * W_TILE; };
+  auto slot_of = [&](int w) -> uint32_t { return (wb + (uint32_t)w) % NS; };
+  auto a_at = [&](uint32_t sl) { return lds + sl * A_TILE; };
+  auto w_at = [&](uint32_t sl) { return lds + W_BASE + sl * W_TILE; };
+  auto a_slot = [&](int w) { return a_at(slot_of(w)); };
+  auto w_slot = [&](int w) { return w_at(slot_of(w)); };
   // one line of window w's tile of tile `r` (ring slot of window w of the current tile
   // numbering): part 0 = activation tile, part 1 = weight tile
   // lane offsets of the tile loads: {a even, a odd, w even, w odd}
@@ -635,24 +644,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     one(W_CPR, p.w_row_bytes, d.w0, d.w1);
     return d;
   };
-  auto issue_line_of = [&](const TileRes& r, const DmaOffs& vo, int slot_w, int w, auto part_tag, int j) {
+  // one line of window w (K offset) of tile `r` into ring slot sl
+  auto issue_line_of = [&](const TileRes& r, const DmaOffs& vo, uint32_t sl, int w, auto part_tag, int j) {
     constexpr int PART = decltype(part_tag)::value;
     if constexpr (PART == 0) {
       const uint32_t line = wave * A_LINES + j;
-      load_line_to_lds(r.a, a_slot(slot_w) + line * 1024, (line & 1) ? vo.a1 : vo.a0,
+      load_line_to_lds(r.a, a_at(sl) + line * 1024, (line & 1) ? vo.a1 : vo.a0,
                        (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
     } else {
       const uint32_t line = wave * W_LINES + j;
-      load_line_to_lds(r.w, w_slot(slot_w) + line * 1024, (line & 1) ? vo.w1 : vo.w0,
+      load_line_to_lds(r.w, w_at(sl) + line * 1024, (line & 1) ? vo.w1 : vo.w0,
                        (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
     }
   };
-  auto issue_line = [&](int w, auto part_tag, int j) { issue_line_of(cur, voffs, w, w, part_tag, j); };
+  auto issue_line_s = [&](uint32_t sl, int w, auto part_tag, int j) { issue_line_of(cur, voffs, sl, w, part_tag, j); };
   auto issue_loads_with = [&](const DmaOffs& vo, int w) {
 #pragma unroll
-    for (int j = 0; j < A_LINES; ++j) issue_line_of(cur, vo, w, w, std::integral_constant<int, 0>{}, j);
+    for (int j = 0; j < A_LINES; ++j) issue_line_of(cur, vo, slot_of(w), w, std::integral_constant<int, 0>{}, j);
 #pragma unroll
-    for (int j = 0; j < W_LINES; ++j) issue_line_of(cur, vo, w, w, std::integral_constant<int, 1>{}, j);
+    for (int j = 0; j < W_LINES; ++j) issue_line_of(cur, vo, slot_of(w), w, std::integral_constant<int, 1>{}, j);
   };
   auto issue_loads = [&](int w) { issue_loads_with(voffs, w); };
   // scale chunk c (windows c*CW ..) of tile `r` into scale slot (cb + slot_c) & 1
@@ -736,12 +746,15 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   TileRes nxt = cur;
   bool has_next = false;
   int t_next = 0;
-  auto window = [&](int w, auto pend_tag, auto steady_tag, auto next_tag) {
+  // sl: ring slot of window w, a std::integral_constant where the caller knows it (the
+  // slot arithmetic and the read addresses then fold into constants and immediates)
+  auto window = [&](int w, auto pend_tag, auto steady_tag, auto next_tag, auto sl) {
     constexpr bool PEND = decltype(pend_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
     constexpr bool NEXT = decltype(next_tag)::value;
-    const uint8_t* la = a_slot(w);
-    const uint8_t* lw = w_slot(w);
+    const uint32_t s0 = (uint32_t)sl, s1 = (s0 + 1) % NS, sp = (s0 + NS - 1) % NS;
+    const uint8_t* la = a_at(s0);
+    const uint8_t* lw = w_at(s0);
     if constexpr (HAS_SC)
       if (chunk_due(w)) issue_chunk(w / CW + 1);
     if constexpr (NEXT) {
@@ -759,9 +772,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
         for (int k = 0; k + 1 < NS; ++k) {
           if (k < nwin) {
 #pragma unroll
-            for (int j = 0; j < A_LINES; ++j) issue_line_of(nxt, fo, nwin + k, k, I0{}, j);
+            for (int j = 0; j < A_LINES; ++j) issue_line_of(nxt, fo, slot_of(nwin + k), k, I0{}, j);
 #pragma unroll
-            for (int j = 0; j < W_LINES; ++j) issue_line_of(nxt, fo, nwin + k, k, I1{}, j);
+            for (int j = 0; j < W_LINES; ++j) issue_line_of(nxt, fo, slot_of(nwin + k), k, I1{}, j);
           }
         }
       }
@@ -770,7 +783,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     // step-0 tile loads, spread over the reads of step 0
     auto pend_loads = [&](int k) {
       if constexpr (PEND) {
-        if (dma_after(k, VM1, RD) > 0) issue_line(w + NS - 1, I1{}, k * VM1 / RD);
+        if (dma_after(k, VM1, RD) > 0) issue_line_s(sp, w + NS - 1, I1{}, k * VM1 / RD);
       }
     };
     // Steps 0 .. STEPS-2, one scheduling region each (a region boundary after every step
@@ -829,9 +842,9 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     stage_barrier();                      // every wave is past stage `cur`
     __builtin_amdgcn_sched_barrier(0);
     // refill the slot just released, spread over the next window's step-0 reads
-    read_frags<MODE>(f0, a_slot(w + 1), w_slot(w + 1), wm, wn, lane, 0, [&](int k) {
+    read_frags<MODE>(f0, a_at(s1), w_at(s1), wm, wn, lane, 0, [&](int k) {
       if constexpr (STEADY) {
-        if (dma_after(k, VM0, RD) > 0) issue_line(w + NS, I0{}, k * VM0 / RD);
+        if (dma_after(k, VM0, RD) > 0) issue_line_s(s0, w + NS, I0{}, k * VM0 / RD);
       }
     });
     if constexpr (C::STEPS == 4)
@@ -865,13 +878,31 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     has_next = kPersistent<MODE> && t_next < nt;
     int w = 0;
     if (nwin > NS) {
-      window(0, F_{}, T_{}, F_{});
-      for (w = 1; w < nwin - NS; ++w) window(w, T_{}, T_{}, F_{});
-      window(w, T_{}, F_{}, F_{});
+      window(0, F_{}, T_{}, F_{}, slot_of(0));
+      w = 1;
+      // steady windows NS at a time, each with its ring slot a constant (wb = 0 without
+      // persistent workgroups)
+      auto steady_groups = [&](auto wb_tag) {
+        constexpr uint32_t WB = decltype(wb_tag)::value;
+        auto one = [&](auto u_tag) {
+          constexpr int U = decltype(u_tag)::value;
+          if constexpr (U < NS) window(w + U, T_{}, T_{}, F_{}, std::integral_constant<uint32_t, (WB + 1 + U) % NS>{});
+        };
+        for (; w + NS <= nwin - NS; w += NS) {
+          one(std::integral_constant<int, 0>{});
+          one(std::integral_constant<int, 1>{});
+          one(std::integral_constant<int, 2>{});
+        }
+      };
+      // (persistent W4A4 keeps one runtime-slot loop: constant-slot instances per first slot
+      // hold more addresses live than its registers allow)
+      if constexpr (!kPersistent<MODE>) steady_groups(std::integral_constant<uint32_t, 0>{});
+      for (; w < nwin - NS; ++w) window(w, T_{}, T_{}, F_{}, slot_of(w));
+      window(w, T_{}, F_{}, F_{}, slot_of(w));
       ++w;
     }
-    for (; w < nwin - 1; ++w) window(w, F_{}, F_{}, F_{});
-    window(nwin - 1, F_{}, F_{}, T_{});
+    for (; w < nwin - 1; ++w) window(w, F_{}, F_{}, F_{}, slot_of(w));
+    window(nwin - 1, F_{}, F_{}, T_{}, slot_of(nwin - 1));
 
     // ---- epilogue: fp32 -> bf16 (RNE) ----
     const uint32_t el = lane_here();
@@ -932,6 +963,19 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     read_scales(0, scw, sca);
   }
 }
+
+}  // namespace
+
+#if defined(MXQ_GEMM_W4A8_OBJECT)
+// The W4A8 instance, launched from launch_gemm in the main object.
+void launch_fast_w4a8(const Params& p, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A8>, dim3(grid), dim3(NT), 0, stream, p);
+}
+#else
+// Defined in the W4A8 object (gemm_w4a8.hip: this file, built with machine sinking off).
+void launch_fast_w4a8(const Params& p, unsigned grid, hipStream_t stream);
+
+namespace {
 
 // ---------------------------------------------------------------------------------
 // W4A4 with the dynamic activation quantization fused in ("AMD Quark adds native W4A8
@@ -1821,8 +1865,11 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
         // workgroup maps to its XCD), or one per tile when there are fewer tiles
         const int cus = kPersistent<MD> ? device_cu_count() & ~7 : 0;
         const int nt = p.tiles_m * p.tiles_n;
-        const dim3 pgrid((unsigned)(cus > 0 && cus < nt ? cus : nt));
-        hipLaunchKernelGGL(gemm_fast_kernel<MD>, pgrid, block, 0, stream, p);
+        const unsigned pgrid = (unsigned)(cus > 0 && cus < nt ? cus : nt);
+        if constexpr (MD == GEMM_W4A8)
+          launch_fast_w4a8(p, pgrid, stream);
+        else
+          hipLaunchKernelGGL(gemm_fast_kernel<MD>, dim3(pgrid), block, 0, stream, p);
       }
     } else {
       p.nwin = (int)((K + Cfg<MD>::K_WIN - 1) / Cfg<MD>::K_WIN);
@@ -1891,5 +1938,7 @@ hipError_t launch_gemm_w4a4_fused(const void* a, bool f32, int64_t ld_a, const u
   }
   return hipGetLastError();
 }
+
+#endif  // MXQ_GEMM_W4A8_OBJECT
 
 }  // namespace mxq
