@@ -122,8 +122,8 @@ def algorithmic_bytes(wl, label):
             "mxq_sqnr_w4a8": 4.0 * M * N}[label]
 
 
-SRC_OF = {"mxq_quantize": ("quantize.hip",), "mxq_quantize_fp8": ("quantize.hip",), "mxq_gemm_w4a4": ("gemm.hip",),
-          "mxq_gemm_w4a8": ("gemm.hip", "gemm_w4a8.hip"), "mxq_gemm_bf16": ("gemm.hip",), "mxq_sqnr_w4a4": ("sqnr.hip",),
+SRC_OF = {"mxq_quantize": ("quantize.hip",), "mxq_quantize_fp8": ("quantize.hip",), "mxq_gemm_w4a4": ("gemm.hip", "gemm_scaled.hip"),
+          "mxq_gemm_w4a8": ("gemm.hip", "gemm_scaled.hip"), "mxq_gemm_bf16": ("gemm.hip",), "mxq_sqnr_w4a4": ("sqnr.hip",),
           "mxq_sqnr_w4a8": ("sqnr.hip",)}
 
 

@@ -33,7 +33,6 @@
 //    MFMA throughput on real data than 32 x 32 x 16.
 //  * gemm_w4a4_fused8_kernel takes unquantized activations and quantizes each activation
 //    tile into LDS inside the GEMM, bit-identically to the separate quantizer.
-#include <atomic>
 #include <type_traits>
 #include <utility>
 
@@ -93,15 +92,6 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// The lane index, re-derived where it is called: the asm statement cannot be moved, so
-// address arithmetic built on it stays where it is used (a persistent kernel's epilogue
-// addresses would otherwise be hoisted out of the tile loop and held across the K loop).
-__device__ __forceinline__ uint32_t lane_here() {
-  uint32_t l;
-  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
-  return l;
-}
-
 // Column of byte `col` (0..31) of a row of a 32-byte-per-row scale chunk in LDS, for a row
 // whose index within its 32-row line is r: rows with bit 2 set hold their 16-byte halves
 // swapped (the chunk loads place them so).
@@ -109,8 +99,8 @@ __device__ __forceinline__ uint32_t sc_col(uint32_t col, uint32_t r) { return co
 
 }  // namespace
 
-// Kernel arguments of every GEMM kernel here (named, so that the W4A8 object built from
-// this file with MXQ_GEMM_W4A8_OBJECT shares the type with its launcher).
+// Kernel arguments of every GEMM kernel here (named, so that the scaled-GEMM object built
+// from this file with MXQ_GEMM_SCALED_OBJECT shares the type with its launcher).
 struct Params {
   const uint8_t* a;
   const uint8_t* a_scales;
@@ -507,15 +497,6 @@ __device__ __forceinline__ void store_partial_tile(const Params& p, const v16f (
   }
 }
 
-// Whether gemm_fast_kernel<MODE> runs persistent workgroups (a grid of at most one
-// workgroup per compute unit, each looping over tiles).  W4A4 gains from overlapping each
-// tile's epilogue and the next tile's first loads (3-4 % on the FLUX and Wan shapes); in
-// the W4A8 build the loop's live state pushes per-tile spill reloads onto memory waits
-// and it loses 4-6 %, so W4A8 launches one workgroup per tile (the loop then runs once
-// and the next-tile code folds away).
-template <int MODE>
-constexpr bool kPersistent = MODE == GEMM_W4A4;
-
 template <int MODE>
 __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   using C = Fast<MODE>;
@@ -547,41 +528,25 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   const uint32_t wave = (uint32_t)__builtin_amdgcn_readfirstlane((int)(tid >> 6));
   const uint32_t wm = wave & 1, wn = wave >> 1;
 
-  // Persistent workgroups: workgroup b runs tiles b, b + G, b + 2G, ... (G = gridDim.x, a
-  // multiple of 8 whenever it is below the tile count).  The hardware places workgroup b
-  // on XCD b mod 8, and so is every tile it runs; the XCD-aware raster below hands the
-  // workgroups of one XCD consecutive runs of the grouped tile order, round after round.
   const int nt = p.tiles_m * p.tiles_n;
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7, local = bid >> 3;
   const int q8 = nt >> 3, r8 = nt & 7;
-  auto tile_origin_of = [&](int t, int& m0_, int& n0_) {
-    const int xcd = t & 7, local = t >> 3;
-    const int seq = xcd * q8 + min(xcd, r8) + local;
-    const int group = seq / (GROUP_M * p.tiles_n);
-    const int first_m = group * GROUP_M;
-    const int gm = min(GROUP_M, p.tiles_m - first_m);
-    const int in_group = seq - group * GROUP_M * p.tiles_n;
-    m0_ = (first_m + in_group % gm) * BM;
-    n0_ = (in_group / gm) * BN;
-  };
+  const int seq = xcd * q8 + min(xcd, r8) + local;
+  const int group = seq / (GROUP_M * p.tiles_n);
+  const int first_m = group * GROUP_M;
+  const int gm = min(GROUP_M, p.tiles_m - first_m);
+  const int in_group = seq - group * GROUP_M * p.tiles_n;
+  const int tm = first_m + in_group % gm, tn = in_group / gm;
+  const int m0 = tm * BM, n0 = tn * BN;
+
   constexpr bool has_as = MODE == GEMM_W4A4;
-  // buffer resources of one tile: activation rows, weight rows and their scale rows
-  struct TileRes {
-    __amdgpu_buffer_rsrc_t a, w, sw, sa;
-  };
-  auto tile_res = [&](int m0_, int n0_) {
-    const uint32_t rows_a = (uint32_t)min(BM, p.M - m0_), rows_w = (uint32_t)min(BN, p.N - n0_);
-    TileRes r;
-    r.a = make_rsrc(p.a + (int64_t)m0_ * p.a_row_bytes, rows_a * p.a_row_bytes);
-    r.w = make_rsrc(p.w + (int64_t)n0_ * p.w_row_bytes, rows_w * p.w_row_bytes);
-    r.sw = make_rsrc(p.w_scales + (int64_t)n0_ * p.scale_row_bytes, rows_w * p.scale_row_bytes);
-    r.sa = make_rsrc(has_as ? p.a_scales + (int64_t)m0_ * p.scale_row_bytes : p.a,
-                     has_as ? rows_a * p.scale_row_bytes : 0);
-    return r;
-  };
-  int t = blockIdx.x;
-  int m0, n0;
-  tile_origin_of(t, m0, n0);
-  TileRes cur = tile_res(m0, n0);
+  const uint32_t rows_a = (uint32_t)min(BM, p.M - m0), rows_w = (uint32_t)min(BN, p.N - n0);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a + (int64_t)m0 * p.a_row_bytes, rows_a * p.a_row_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w + (int64_t)n0 * p.w_row_bytes, rows_w * p.w_row_bytes);
+  const __amdgpu_buffer_rsrc_t rsw = make_rsrc(p.w_scales + (int64_t)n0 * p.scale_row_bytes, rows_w * p.scale_row_bytes);
+  const __amdgpu_buffer_rsrc_t rsa =
+      make_rsrc(has_as ? p.a_scales + (int64_t)m0 * p.scale_row_bytes : p.a, has_as ? rows_a * p.scale_row_bytes : 0);
 
   // Lane geometry of the direct-to-LDS tile loads: LDS line q holds rows
   // [q * ROWS_PER_LINE, ...); lane i lands at byte 16 i of the line, i.e. in row i / CPR at
@@ -608,79 +573,39 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
 
   // A window's tile loads in two parts, issued under different MFMA steps so that the
   // four waves never queue a whole window of DMA at once: part 0 = activation tile,
-  // part 1 = weight tile.
-  // Ring slots: window w of the current tile lives in tile slot (wb + w) mod NS, its scale
-  // chunk c in scale slot (cb + c) & 1; wb and cb advance by the tile's window and chunk
-  // counts from tile to tile, so the next tile's first windows fill the slots the current
-  // tile's last windows leave free.
-  uint32_t wb = 0, cb = 0;
-  auto slot_of = [&](int w) -> uint32_t { return (wb + (uint32_t)w) % NS; };
+  // part 1 = weight tile.  Window w lives in ring slot w mod NS.
   auto a_at = [&](uint32_t sl) { return lds + sl * A_TILE; };
   auto w_at = [&](uint32_t sl) { return lds + W_BASE + sl * W_TILE; };
-  auto a_slot = [&](int w) { return a_at(slot_of(w)); };
-  auto w_slot = [&](int w) { return w_at(slot_of(w)); };
-  // one line of window w's tile of tile `r` (ring slot of window w of the current tile
-  // numbering): part 0 = activation tile, part 1 = weight tile
-  // lane offsets of the tile loads: {a even, a odd, w even, w odd}
-  struct DmaOffs {
-    uint32_t a0, a1, w0, w1;
-  };
-  const DmaOffs voffs{a_voff0, a_voff1, w_voff0, w_voff1};
-  // the same offsets computed afresh, for the once-per-tile loads (the long-lived copies
-  // may sit in scratch there, and a reload would wait for every load in flight)
-  auto fresh_voffs = [&]() {
-    const uint32_t l = lane_here();
-    auto one = [&](uint32_t cpr, uint32_t row_bytes, uint32_t& even, uint32_t& odd) {
-      const uint32_t row = l / cpr, slot = l % cpr;
-      if (cpr == 8) {
-        even = row * row_bytes + ((slot ^ ((row >> 1) & 7u)) * 16);
-        odd = row * row_bytes + ((slot ^ (((8u + row) >> 1) & 7u)) * 16);
-      } else {
-        even = odd = row * row_bytes + ((slot ^ ((row >> 2) & 3u)) * 16);
-      }
-    };
-    DmaOffs d;
-    one(A_CPR, p.a_row_bytes, d.a0, d.a1);
-    one(W_CPR, p.w_row_bytes, d.w0, d.w1);
-    return d;
-  };
-  // one line of window w (K offset) of tile `r` into ring slot sl
-  auto issue_line_of = [&](const TileRes& r, const DmaOffs& vo, uint32_t sl, int w, auto part_tag, int j) {
+  // one line of window w's tile into ring slot sl
+  auto issue_line = [&](uint32_t sl, int w, auto part_tag, int j) {
     constexpr int PART = decltype(part_tag)::value;
     if constexpr (PART == 0) {
       const uint32_t line = wave * A_LINES + j;
-      load_line_to_lds(r.a, a_at(sl) + line * 1024, (line & 1) ? vo.a1 : vo.a0,
+      load_line_to_lds(ra, a_at(sl) + line * 1024, (line & 1) ? a_voff1 : a_voff0,
                        (uint32_t)w * C::A_RB + line * A_ROWS_PER_LINE * p.a_row_bytes);
     } else {
       const uint32_t line = wave * W_LINES + j;
-      load_line_to_lds(r.w, w_at(sl) + line * 1024, (line & 1) ? vo.w1 : vo.w0,
+      load_line_to_lds(rw, w_at(sl) + line * 1024, (line & 1) ? w_voff1 : w_voff0,
                        (uint32_t)w * C::W_RB + line * W_ROWS_PER_LINE * p.w_row_bytes);
     }
   };
-  auto issue_line_s = [&](uint32_t sl, int w, auto part_tag, int j) { issue_line_of(cur, voffs, sl, w, part_tag, j); };
-  auto issue_loads_with = [&](const DmaOffs& vo, int w) {
+  auto issue_loads = [&](int w) {
 #pragma unroll
-    for (int j = 0; j < A_LINES; ++j) issue_line_of(cur, vo, slot_of(w), w, std::integral_constant<int, 0>{}, j);
+    for (int j = 0; j < A_LINES; ++j) issue_line((uint32_t)w % NS, w, std::integral_constant<int, 0>{}, j);
 #pragma unroll
-    for (int j = 0; j < W_LINES; ++j) issue_line_of(cur, vo, slot_of(w), w, std::integral_constant<int, 1>{}, j);
+    for (int j = 0; j < W_LINES; ++j) issue_line((uint32_t)w % NS, w, std::integral_constant<int, 1>{}, j);
   };
-  auto issue_loads = [&](int w) { issue_loads_with(voffs, w); };
-  // scale chunk c (windows c*CW ..) of tile `r` into scale slot (cb + slot_c) & 1
+  // scale chunk c (windows c*CW ..) into scale slot c & 1
   const int nchunks = (p.nwin + CW - 1) / CW;
-  auto issue_chunk_of = [&](const TileRes& r, uint32_t sc_vo, int slot_c, int c) {
-    uint8_t* slot = lds + SC_BASE + ((cb + (uint32_t)slot_c) & 1u) * SLOT;
+  auto issue_chunk = [&](int c) {
+    uint8_t* slot = lds + SC_BASE + (uint32_t)(c & 1) * SLOT;
 #pragma unroll
     for (int j = 0; j < SC_LINES; ++j) {
       const uint32_t line = wave * SC_LINES + j;
       const bool is_w = line < BN / 32;
       const uint32_t row0 = (is_w ? line : line - BN / 32) * 32;
-      load_line_to_lds(is_w ? r.sw : r.sa, slot + line * 1024, sc_vo, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
+      load_line_to_lds(is_w ? rsw : rsa, slot + line * 1024, sc_voff, (uint32_t)c * SC_ROW + row0 * p.scale_row_bytes);
     }
-  };
-  auto issue_chunk = [&](int c) { issue_chunk_of(cur, sc_voff, c, c); };
-  auto fresh_sc_voff = [&]() {
-    const uint32_t l = lane_here();
-    return (l >> 1) * p.scale_row_bytes + (((l & 1) ^ ((l >> 3) & 1)) * 16);
   };
   // Chunk c+1 goes out at the start of window c*CW (c >= 1; chunk 1 in the prologue): the
   // barrier that ended window c*CW - 1 follows every wave's last read of chunk c-1, the
@@ -695,7 +620,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     if constexpr (HAS_SC) {
       // lane group g's blocks g*STEPS .. g*STEPS+STEPS-1 as bytes 0.. of one word; the
       // window's column (bits 2-4 of the row offset) enters as one XOR with sc_lane
-      const uint8_t* slot = lds + SC_BASE + ((cb + (uint32_t)(w / CW)) & 1u) * SLOT;
+      const uint8_t* slot = lds + SC_BASE + (uint32_t)((w / CW) & 1) * SLOT;
       const uint32_t off = sc_lane ^ ((uint32_t)(w % CW) * SC_WIN);
       const uint32_t sh = (SC_WIN == 8) ? 0 : 16 * (lane >> 5);
 #pragma unroll
@@ -710,6 +635,13 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   };
 
   v16f acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
   const int nwin = p.nwin;
   uint32_t scw[4] = {0, 0, 0, 0}, sca[4] = {0, 0, 0, 0};
   v4i f0[12], f1[12];
@@ -732,7 +664,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
 #pragma unroll
   for (int k = 1; k < NS; ++k)
     if (k < nwin) issue_loads(k);
-  read_frags<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
+  read_frags<MODE>(f0, a_at(0), w_at(0), wm, wn, lane, 0);
   read_scales(0, scw, sca);
 
   // One window.  PEND: the step-0 tile loads go out (the weight tile of window w+NS-1,
@@ -740,50 +672,24 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   // waits for window w+1 only and refills the slot this window releases with the
   // activation tile of window w+NS.  The tail waits for everything and loads no tiles.
   // Memory-free MFMAs cannot be sunk past the barrier: every step is its own scheduling
-  // region.
+  // region.  sl is window w's ring slot w mod NS, a std::integral_constant where the
+  // caller knows it: the slot arithmetic and the LDS read addresses then fold into
+  // constants and instruction offsets.
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
-  TileRes nxt = cur;
-  bool has_next = false;
-  int t_next = 0;
-  // sl: ring slot of window w, a std::integral_constant where the caller knows it (the
-  // slot arithmetic and the read addresses then fold into constants and immediates)
-  auto window = [&](int w, auto pend_tag, auto steady_tag, auto next_tag, auto sl) {
+  auto window = [&](int w, auto pend_tag, auto steady_tag, auto sl) {
     constexpr bool PEND = decltype(pend_tag)::value;
     constexpr bool STEADY = decltype(steady_tag)::value;
-    constexpr bool NEXT = decltype(next_tag)::value;
     const uint32_t s0 = (uint32_t)sl, s1 = (s0 + 1) % NS, sp = (s0 + NS - 1) % NS;
     const uint8_t* la = a_at(s0);
     const uint8_t* lw = w_at(s0);
     if constexpr (HAS_SC)
       if (chunk_due(w)) issue_chunk(w / CW + 1);
-    if constexpr (NEXT) {
-      // Last window: the next tile's windows 0 .. NS-2 go to the slots after this one (free
-      // since the hand-overs of windows nwin-NS .. nwin-2) and its scale chunk 0 to the
-      // scale slot after this tile's last chunk (free since that chunk's predecessor was
-      // last read).  Each is older than the hand-over's full wait below.
-      if (has_next) {
-        int m0n, n0n;
-        tile_origin_of(t_next, m0n, n0n);
-        nxt = tile_res(m0n, n0n);
-        if constexpr (HAS_SC) issue_chunk_of(nxt, fresh_sc_voff(), nchunks, 0);
-        const DmaOffs fo = fresh_voffs();
-#pragma unroll
-        for (int k = 0; k + 1 < NS; ++k) {
-          if (k < nwin) {
-#pragma unroll
-            for (int j = 0; j < A_LINES; ++j) issue_line_of(nxt, fo, slot_of(nwin + k), k, I0{}, j);
-#pragma unroll
-            for (int j = 0; j < W_LINES; ++j) issue_line_of(nxt, fo, slot_of(nwin + k), k, I1{}, j);
-          }
-        }
-      }
-    }
     __builtin_amdgcn_sched_barrier(0);
     // step-0 tile loads, spread over the reads of step 0
     auto pend_loads = [&](int k) {
       if constexpr (PEND) {
-        if (dma_after(k, VM1, RD) > 0) issue_line_s(sp, w + NS - 1, I1{}, k * VM1 / RD);
+        if (dma_after(k, VM1, RD) > 0) issue_line(sp, w + NS - 1, I1{}, k * VM1 / RD);
       }
     };
     // Steps 0 .. STEPS-2, one scheduling region each (a region boundary after every step
@@ -844,7 +750,7 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
     // refill the slot just released, spread over the next window's step-0 reads
     read_frags<MODE>(f0, a_at(s1), w_at(s1), wm, wn, lane, 0, [&](int k) {
       if constexpr (STEADY) {
-        if (dma_after(k, VM0, RD) > 0) issue_line_s(s0, w + NS, I0{}, k * VM0 / RD);
+        if (dma_after(k, VM0, RD) > 0) issue_line(s0, w + NS, I0{}, k * VM0 / RD);
       }
     });
     if constexpr (C::STEPS == 4)
@@ -867,53 +773,36 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
   };
   using T_ = std::true_type;
   using F_ = std::false_type;
-  for (;;) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-    t_next = t + (int)gridDim.x;
-    has_next = kPersistent<MODE> && t_next < nt;
-    int w = 0;
-    if (nwin > NS) {
-      window(0, F_{}, T_{}, F_{}, slot_of(0));
-      w = 1;
-      // steady windows NS at a time, each with its ring slot a constant (wb = 0 without
-      // persistent workgroups)
-      auto steady_groups = [&](auto wb_tag) {
-        constexpr uint32_t WB = decltype(wb_tag)::value;
-        auto one = [&](auto u_tag) {
-          constexpr int U = decltype(u_tag)::value;
-          if constexpr (U < NS) window(w + U, T_{}, T_{}, F_{}, std::integral_constant<uint32_t, (WB + 1 + U) % NS>{});
-        };
-        for (; w + NS <= nwin - NS; w += NS) {
-          one(std::integral_constant<int, 0>{});
-          one(std::integral_constant<int, 1>{});
-          one(std::integral_constant<int, 2>{});
-        }
-      };
-      // (persistent W4A4 keeps one runtime-slot loop: constant-slot instances per first slot
-      // hold more addresses live than its registers allow)
-      if constexpr (!kPersistent<MODE>) steady_groups(std::integral_constant<uint32_t, 0>{});
-      for (; w < nwin - NS; ++w) window(w, T_{}, T_{}, F_{}, slot_of(w));
-      window(w, T_{}, F_{}, F_{}, slot_of(w));
-      ++w;
+  auto slot_of = [](int w) { return (uint32_t)w % NS; };
+  int w = 0;
+  if (nwin > NS) {
+    window(0, F_{}, T_{}, slot_of(0));
+    // steady windows NS at a time, window 1 + NS k + u in the constant slot (1 + u) mod NS
+    auto one = [&](auto u_tag) {
+      constexpr int U = decltype(u_tag)::value;
+      if constexpr (U < NS) window(w + U, T_{}, T_{}, std::integral_constant<uint32_t, (1 + U) % NS>{});
+    };
+    static_assert(NS <= 3, "one() covers three steady windows per group");
+    for (w = 1; w + NS <= nwin - NS; w += NS) {
+      one(std::integral_constant<int, 0>{});
+      one(std::integral_constant<int, 1>{});
+      one(std::integral_constant<int, 2>{});
     }
-    for (; w < nwin - 1; ++w) window(w, F_{}, F_{}, F_{}, slot_of(w));
-    window(nwin - 1, F_{}, F_{}, T_{}, slot_of(nwin - 1));
+    for (; w < nwin - NS; ++w) window(w, T_{}, T_{}, slot_of(w));
+    window(w, T_{}, F_{}, slot_of(w));
+    ++w;
+  }
+  for (; w < nwin; ++w) window(w, F_{}, F_{}, slot_of(w));
 
-    // ---- epilogue: fp32 -> bf16 (RNE) ----
-    const uint32_t el = lane_here();
-    if (p.vec16 && n0 + BN <= p.N) {
+  // ---- epilogue: fp32 -> bf16 (RNE) ----
+  if (p.vec16 && n0 + BN <= p.N) {
       // A lane holds 4 consecutive columns of 32 different rows, so a direct store touches
       // 32 cache lines per instruction.  Each wave instead parks 32 rows of its 128 x 128
       // sub-tile at a time in its own 8 KB of the last window's activation slot (free after
       // the last hand-over barrier; 16-byte chunk c of row r at slot c ^ (r & 15), spreading
       // the writes of 16 rows over all banks) and stores 4 whole 256-byte row segments per
-      // instruction.  The stores drain under the next tile's first window.
-      uint8_t* sub = a_slot(nwin - 1) + wave * (32u * 256u);
+      // instruction.
+      uint8_t* sub = a_at(slot_of(nwin - 1)) + wave * (32u * 256u);
       const int mw = m0 + (int)wm * 128;
       uint16_t* obase = p.out + (int64_t)mw * p.ld_out + n0 + wn * 128;
 #pragma unroll
@@ -930,49 +819,38 @@ __global__ __launch_bounds__(NT, 1) void gemm_fast_kernel(Params p) {
               v2 *= p.a_scale;
               v3 *= p.a_scale;
             }
-            const uint32_t chunk = 4 * i + pp, er = el & 31;
-            *reinterpret_cast<v2u*>(sub + er * 256 + ((chunk ^ (er & 15)) << 4) + 8 * (el >> 5)) =
+            const uint32_t chunk = 4 * i + pp, er = lane & 31;
+            *reinterpret_cast<v2u*>(sub + er * 256 + ((chunk ^ (er & 15)) << 4) + 8 * (lane >> 5)) =
                 v2u{pack_bf16x2(v0, v1), pack_bf16x2(v2, v3)};
             if (pp == 3) __builtin_amdgcn_sched_barrier(0);
           }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-          const uint32_t row = 4 * q + (el >> 4), c = el & 15;
+          const uint32_t row = 4 * q + (lane >> 4), c = lane & 15;
           const v4i v = *reinterpret_cast<const v4i*>(sub + row * 256 + ((c ^ (row & 15)) << 4));
           const int orow = 32 * j + (int)row;
           if (mw + orow < p.M) *reinterpret_cast<v4i*>(obase + (int64_t)orow * p.ld_out + c * 8) = v;
         }
       }
-    } else {
-      store_partial_tile<MODE>(p, acc, el, wm, wn, m0, n0);
-    }
-    if (!has_next) break;
-    // Next tile: its window 0 and scale chunk 0 are resident (the last hand-over waited for
-    // them); once every wave has read its staged rows back, window NS-1 may refill the last
-    // window's slot and chunk 1 the last chunk's scale slot.
-    stage_barrier();
-    wb = (wb + (uint32_t)nwin) % NS;
-    cb = (cb + (uint32_t)nchunks) & 1u;
-    t = t_next;
-    tile_origin_of(t, m0, n0);
-    cur = nxt;
-    if constexpr (HAS_SC)
-      if (nchunks > 1) issue_chunk_of(cur, fresh_sc_voff(), 1, 1);
-    if (NS - 1 < nwin) issue_loads_with(fresh_voffs(), NS - 1);
-    read_frags<MODE>(f0, a_slot(0), w_slot(0), wm, wn, lane, 0);
-    read_scales(0, scw, sca);
+  } else {
+    store_partial_tile<MODE>(p, acc, lane, wm, wn, m0, n0);
   }
 }
 
 }  // namespace
 
-#if defined(MXQ_GEMM_W4A8_OBJECT)
-// The W4A8 instance, launched from launch_gemm in the main object.
+#if defined(MXQ_GEMM_SCALED_OBJECT)
+// The scaled instances, launched from launch_gemm in the main object.
+void launch_fast_w4a4(const Params& p, unsigned grid, hipStream_t stream) {
+  hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A4>, dim3(grid), dim3(NT), 0, stream, p);
+}
 void launch_fast_w4a8(const Params& p, unsigned grid, hipStream_t stream) {
   hipLaunchKernelGGL(gemm_fast_kernel<GEMM_W4A8>, dim3(grid), dim3(NT), 0, stream, p);
 }
 #else
-// Defined in the W4A8 object (gemm_w4a8.hip: this file, built with machine sinking off).
+// Defined in the scaled-GEMM object (gemm_scaled.hip: this file, built with machine
+// sinking off).
+void launch_fast_w4a4(const Params& p, unsigned grid, hipStream_t stream);
 void launch_fast_w4a8(const Params& p, unsigned grid, hipStream_t stream);
 
 namespace {
@@ -1808,20 +1686,6 @@ __global__ __launch_bounds__(NT8, 1) void gemm_w4a4_fused8_kernel(Params p) {
   }
 }
 
-// Compute units of the current device (the persistent kernels' grid), read once per device.
-int device_cu_count() {
-  constexpr int kMaxDevices = 64;
-  static std::atomic<int> cache[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
-
 }  // namespace
 
 hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, const void* w,
@@ -1860,16 +1724,10 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
       // for bit (eight waves of 32 x 32 MFMAs measured slower for both scaled modes)
       if constexpr (MD == GEMM_BF16) {
         hipLaunchKernelGGL(gemm_bf16_kernel, grid, dim3(NT16), 0, stream, p);
+      } else if constexpr (MD == GEMM_W4A4) {
+        launch_fast_w4a4(p, grid.x, stream);
       } else {
-        // one persistent workgroup per compute unit (a multiple of 8, so every tile of a
-        // workgroup maps to its XCD), or one per tile when there are fewer tiles
-        const int cus = kPersistent<MD> ? device_cu_count() & ~7 : 0;
-        const int nt = p.tiles_m * p.tiles_n;
-        const unsigned pgrid = (unsigned)(cus > 0 && cus < nt ? cus : nt);
-        if constexpr (MD == GEMM_W4A8)
-          launch_fast_w4a8(p, pgrid, stream);
-        else
-          hipLaunchKernelGGL(gemm_fast_kernel<MD>, dim3(pgrid), block, 0, stream, p);
+        launch_fast_w4a8(p, grid.x, stream);
       }
     } else {
       p.nwin = (int)((K + Cfg<MD>::K_WIN - 1) / Cfg<MD>::K_WIN);
@@ -1939,6 +1797,6 @@ hipError_t launch_gemm_w4a4_fused(const void* a, bool f32, int64_t ld_a, const u
   return hipGetLastError();
 }
 
-#endif  // MXQ_GEMM_W4A8_OBJECT
+#endif  // MXQ_GEMM_SCALED_OBJECT
 
 }  // namespace mxq

@@ -54,7 +54,7 @@ def test_traffic_only_from_a_summary_of_the_same_source(tmp_path, monkeypatch):
         "kernel: k\nsource_sha256_16: 0123456789abcdef\nhbm_bytes_per_launch: 1.5000e+09\n")
     src = tmp_path / "mxfp4_microscaled_quantization_amd" / "csrc"
     src.mkdir(parents=True)
-    for name in ("gemm.hip", "gemm_w4a8.hip"):
+    for name in ("gemm.hip", "gemm_scaled.hip"):
         (src / name).write_bytes(open(os.path.join(ROOT, "mxfp4_microscaled_quantization_amd", "csrc", name),
                                       "rb").read())
     monkeypatch.setattr(bench, "ROOT", str(tmp_path))
