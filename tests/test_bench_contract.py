@@ -46,7 +46,7 @@ def test_cpu_baseline_record():
 
 
 def test_traffic_only_from_a_summary_of_the_same_source(tmp_path, monkeypatch):
-    h = bench._src_hash("gemm.hip")
+    h = bench._src_hash(*bench.SRC_OF["mxq_gemm_w4a4"])
     (tmp_path / "profiles").mkdir()
     (tmp_path / "profiles" / "pmc_mxq_gemm_w4a4_wl.txt").write_text(
         f"kernel: k\nsource_sha256_16: {h}\nhbm_bytes_per_launch: 1.5000e+09\n")
