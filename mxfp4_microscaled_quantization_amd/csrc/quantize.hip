@@ -251,15 +251,27 @@ __global__ __launch_bounds__(THREADS) void mx_quantize_rot_kernel(
             v[i] = __fadd_rn(a, c);
             v[i + h] = __fsub_rn(a, c);
           }
-      // stages h = 8, 16, ... across lanes l and l ^ (h / 8); the lower index keeps the sum
+      // Stages h = 8, 16, ... across lanes l and l ^ (h / 8); the lower index keeps the sum.
+      // Both lanes form partner + own', own' = own with its sign flipped in the upper lane:
+      // x_i + x_{i+h} (addition commutes) and x_i + (-x_{i+h}), the same binary32 operation
+      // as x_i - x_{i+h}.  One add per element and stage, the exchange folded into it as a
+      // DPP operand where one DPP pattern reaches the partner.
       auto cross = [&](auto d_tag) {
         constexpr int D = decltype(d_tag)::value;
         if constexpr (D < N / 8) {
-          const bool upper = (lane & D) != 0;
+          const unsigned flip = (lane & D) ? 0x80000000u : 0u;
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float other = lane_xor<D>(v[i], lane);
-            v[i] = upper ? __fsub_rn(other, v[i]) : __fadd_rn(v[i], other);
+            const float own = __uint_as_float(__float_as_uint(v[i]) ^ flip);
+            if constexpr (D == 4) {
+              // lane + 4 for the lower half of each 8 lanes, lane - 4 for the upper half
+              const int b = __float_as_int(v[i]);
+              const float lo = __fadd_rn(__int_as_float(__builtin_amdgcn_mov_dpp(b, 0x104, 0xF, 0xF, true)), own);
+              const float hi = __fadd_rn(__int_as_float(__builtin_amdgcn_mov_dpp(b, 0x114, 0xF, 0xF, true)), own);
+              v[i] = (lane & 4) ? hi : lo;
+            } else {
+              v[i] = __fadd_rn(lane_xor<D>(v[i], lane), own);
+            }
           }
         }
       };
@@ -415,27 +427,40 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* __restrict
 // MXFP4 -> bf16: e2m1(code) * 2^(s - 127).  The product is formed in binary32 (exact:
 // at most 3 significant bits, exponent within binary32's range down to the subnormal
 // 2^-128) and narrowed to bf16 with round to nearest even (exact in range).
+// CONTIG: codes, scales and output are packed rows (offsets are linear in the quarter
+// index); otherwise the row comes from one 32-bit division (quarters < 2^32).
+template <bool CONTIG>
 __global__ __launch_bounds__(kDqThreads) void dequantize_kernel(
     const uint8_t* __restrict__ codes, int64_t ld_codes, const uint8_t* __restrict__ scales,
     int64_t ld_scales, uint16_t* __restrict__ y, int64_t ld_y, uint32_t blocks_per_row,
-    int64_t total_quarters) {
+    uint32_t total_quarters) {
   // each lane takes kDqUnroll quarters (8 elements each) per pass, loads first
-  const int64_t stride = (int64_t)gridDim.x * kDqThreads * kDqUnroll;
-  for (int64_t g0 = (int64_t)blockIdx.x * kDqThreads * kDqUnroll + threadIdx.x; g0 < total_quarters; g0 += stride) {
+  // the pass counter is 64-bit so that it cannot wrap; quarter indices themselves fit 32 bits
+  const uint64_t stride = (uint64_t)gridDim.x * kDqThreads * kDqUnroll;
+  for (uint64_t g0 = (uint64_t)blockIdx.x * kDqThreads * kDqUnroll + threadIdx.x; g0 < total_quarters; g0 += stride) {
     unsigned c[kDqUnroll], s[kDqUnroll];
     int64_t yo[kDqUnroll];
     bool ok[kDqUnroll];
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
-      const int64_t g = g0 + (int64_t)u * kDqThreads;
-      ok[u] = g < total_quarters;
-      const int64_t b = g >> 2;
-      const int q = (int)(g & 3);
-      const uint32_t row = (uint32_t)(b / blocks_per_row);
-      const uint32_t blk = (uint32_t)(b - (int64_t)row * blocks_per_row);
-      c[u] = ok[u] ? *reinterpret_cast<const unsigned*>(codes + (int64_t)row * ld_codes + blk * 16 + q * 4) : 0u;
-      s[u] = ok[u] ? scales[(int64_t)row * ld_scales + blk] : 0u;
-      yo[u] = (int64_t)row * ld_y + blk * 32 + q * 8;
+      const uint64_t g64 = g0 + (uint64_t)u * kDqThreads;
+      ok[u] = g64 < total_quarters;
+      const uint32_t g = ok[u] ? (uint32_t)g64 : 0u;
+      int64_t co, so;
+      if (CONTIG) {
+        co = (int64_t)g * 4;
+        so = g >> 2;
+        yo[u] = (int64_t)g * 8;
+      } else {
+        const uint32_t b = g >> 2, q = g & 3;
+        const uint32_t row = b / blocks_per_row;
+        const uint32_t blk = b - row * blocks_per_row;
+        co = (int64_t)row * ld_codes + blk * 16 + q * 4;
+        so = (int64_t)row * ld_scales + blk;
+        yo[u] = (int64_t)row * ld_y + blk * 32 + q * 8;
+      }
+      c[u] = ok[u] ? *reinterpret_cast<const unsigned*>(codes + co) : 0u;
+      s[u] = ok[u] ? scales[so] : 0u;
     }
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
@@ -474,23 +499,33 @@ int grid_for(int64_t work_items, int64_t per_block) {
 // fl32(e4m3(q) * a_scale)).  v_cvt_pk_f32_fp8 widens two OCP E4M3 bytes exactly to
 // binary32 (NaN for S.1111.111); the product is one binary32 multiply; v_cvt_pk_bf16_f32
 // rounds to nearest even.  A lane owns 8 consecutive codes of a row per unit.
+// CONTIG as in dequantize_kernel (units < 2^32).
+template <bool CONTIG>
 __global__ __launch_bounds__(kDq8Threads) void dequantize_fp8_kernel(const uint8_t* __restrict__ q, int64_t ld_q,
                                                                     float a_scale, uint16_t* __restrict__ y,
                                                                     int64_t ld_y, uint32_t units_per_row,
-                                                                    int64_t total_units) {
-  const int64_t stride = (int64_t)gridDim.x * kDq8Threads * kDq8Unroll;
-  for (int64_t g0 = (int64_t)blockIdx.x * kDq8Threads * kDq8Unroll + threadIdx.x; g0 < total_units; g0 += stride) {
+                                                                    uint32_t total_units) {
+  const uint64_t stride = (uint64_t)gridDim.x * kDq8Threads * kDq8Unroll;
+  for (uint64_t g0 = (uint64_t)blockIdx.x * kDq8Threads * kDq8Unroll + threadIdx.x; g0 < total_units; g0 += stride) {
     v2u c[kDq8Unroll];
     int64_t yo[kDq8Unroll];
     bool ok[kDq8Unroll];
 #pragma unroll
     for (int u = 0; u < kDq8Unroll; ++u) {
-      const int64_t g = g0 + (int64_t)u * kDq8Threads;
-      ok[u] = g < total_units;
-      const uint32_t row = ok[u] ? (uint32_t)(g / units_per_row) : 0u;
-      const uint32_t col = ok[u] ? (uint32_t)(g - (int64_t)row * units_per_row) * 8u : 0u;
-      c[u] = ok[u] ? *reinterpret_cast<const v2u*>(q + (int64_t)row * ld_q + col) : v2u{0u, 0u};
-      yo[u] = (int64_t)row * ld_y + col;
+      const uint64_t g64 = g0 + (uint64_t)u * kDq8Threads;
+      ok[u] = g64 < total_units;
+      const uint32_t g = ok[u] ? (uint32_t)g64 : 0u;
+      int64_t qo;
+      if (CONTIG) {
+        qo = (int64_t)g * 8;
+        yo[u] = qo;
+      } else {
+        const uint32_t row = g / units_per_row;
+        const uint32_t col = (g - row * units_per_row) * 8u;
+        qo = (int64_t)row * ld_q + col;
+        yo[u] = (int64_t)row * ld_y + col;
+      }
+      c[u] = ok[u] ? *reinterpret_cast<const v2u*>(q + qo) : v2u{0u, 0u};
     }
 #pragma unroll
     for (int u = 0; u < kDq8Unroll; ++u) {
@@ -600,22 +635,24 @@ hipError_t launch_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8
                              int64_t ld_scales, int64_t rows, int64_t cols, uint16_t* y, int64_t ld_y,
                              hipStream_t stream) {
   const int64_t bpr = cols / 32;
-  const int64_t total = rows * bpr * 4;
+  const int64_t total = rows * bpr * 4;   // quarters: below 2^32 (the API bounds rows * cols / 8)
   if (total == 0) return hipSuccess;
   const int grid = grid_for(total, kDqThreads * kDqUnroll);
-  hipLaunchKernelGGL(dequantize_kernel, dim3(grid), dim3(kDqThreads), 0, stream, codes, ld_codes, scales,
-                     ld_scales, y, ld_y, (uint32_t)bpr, total);
+  const bool contig = ld_codes == cols / 2 && ld_scales == bpr && ld_y == cols;
+  hipLaunchKernelGGL(contig ? dequantize_kernel<true> : dequantize_kernel<false>, dim3(grid), dim3(kDqThreads), 0,
+                     stream, codes, ld_codes, scales, ld_scales, y, ld_y, (uint32_t)bpr, (uint32_t)total);
   return hipGetLastError();
 }
 
 hipError_t launch_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int64_t rows, int64_t cols,
                                  uint16_t* y, int64_t ld_y, hipStream_t stream) {
   const int64_t upr = cols / 8;
-  const int64_t total = rows * upr;
+  const int64_t total = rows * upr;       // below 2^32 (the API bounds rows * cols / 8)
   if (total == 0) return hipSuccess;
   const int grid = grid_for(total, kDq8Threads * kDq8Unroll);
-  hipLaunchKernelGGL(dequantize_fp8_kernel, dim3(grid), dim3(kDq8Threads), 0, stream, q, ld_q, a_scale, y, ld_y,
-                     (uint32_t)upr, total);
+  const bool contig = ld_q == cols && ld_y == cols;
+  hipLaunchKernelGGL(contig ? dequantize_fp8_kernel<true> : dequantize_fp8_kernel<false>, dim3(grid),
+                     dim3(kDq8Threads), 0, stream, q, ld_q, a_scale, y, ld_y, (uint32_t)upr, (uint32_t)total);
   return hipGetLastError();
 }
 
