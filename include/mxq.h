@@ -182,12 +182,30 @@ mxq_status mxq_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales,
  *            below 2^31 bytes.
  * w_codes, w_scales, out_bf16, ld_out, K : as for mxq_gemm_w4a4.
  * rule     : MXQ_SCALE_OCP or MXQ_SCALE_UOS (as mxq_quantize_rule).
- * Errors as for mxq_quantize_rule and mxq_gemm_w4a4.
+ * workspace, ws_bytes : NULL (0), or device memory of at least
+ *            mxq_gemm_w4a4_fused_workspace_bytes(M, N, K) bytes, 16-byte aligned, owned by
+ *            the caller and not used by anything else until the call's work on `stream` is
+ *            done.  The fused kernel quantizes each activation tile once per 256 output
+ *            columns; past the measured break-even (more than 3 column tiles for K >= 8192,
+ *            more than 1 below) a pass of its own is faster, and with a workspace the call
+ *            then quantizes into it and runs mxq_gemm_w4a4 (the same bits).  With NULL the
+ *            fused kernel always runs.
+ * Errors as for mxq_quantize_rule and mxq_gemm_w4a4; MXQ_ERR_INVALID_ARG for a non-NULL
+ * workspace that is misaligned or smaller than the size above.
  */
 mxq_status mxq_gemm_w4a4_fused(const void* a, mxq_dtype dt, int64_t ld_a,
                                const uint8_t* w_codes, const uint8_t* w_scales,
                                int64_t M, int64_t N, int64_t K, mxq_scale_rule rule,
-                               uint16_t* out_bf16, int64_t ld_out, void* stream);
+                               uint16_t* out_bf16, int64_t ld_out, void* workspace,
+                               size_t ws_bytes, void* stream);
+
+/*
+ * mxq_gemm_w4a4_fused_workspace_bytes -- bytes of workspace with which mxq_gemm_w4a4_fused
+ * takes the separate-quantization route for this shape: 0 where the fused kernel is the
+ * faster (or for an empty or invalid shape), else M * K / 2 rounded up to 16 plus
+ * M * K / 32.  Host only; no device work.
+ */
+size_t mxq_gemm_w4a4_fused_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
 /*
  * mxq_gemm_w4a8 -- out = bf16_RNE( fl32( a_scale * sum_b 2^(SW[n,b] - 127) *

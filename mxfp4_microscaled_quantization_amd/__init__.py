@@ -42,7 +42,8 @@ ABI_SYMBOLS = {
     "mxq_absmax": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _i64, _i64, _ptr, _ptr]),
     "mxq_gemm_w4a4": (ctypes.c_int, [_ptr, _ptr, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_gemm_w4a4_fused": (ctypes.c_int, [_ptr, ctypes.c_int, _i64, _ptr, _ptr, _i64, _i64, _i64, ctypes.c_int, _ptr,
-                                           _i64, _ptr]),
+                                           _i64, _ptr, _sz, _ptr]),
+    "mxq_gemm_w4a4_fused_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "mxq_gemm_w4a8": (ctypes.c_int, [_ptr, _f32, _ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_gemm_bf16": (ctypes.c_int, [_ptr, _ptr, _i64, _i64, _i64, _ptr, _i64, _ptr]),
     "mxq_sqnr_workspace_bytes": (_sz, [_i64]),
@@ -282,15 +283,25 @@ def gemm_w4a4(a_codes, a_scales, w_codes, w_scales, out=None):
     return out
 
 
-def gemm_w4a4_fused(a, w_codes, w_scales, rule: str = "ocp", out=None):
+def fused_workspace_bytes(M: int, N: int, K: int) -> int:
+    """Workspace bytes with which gemm_w4a4_fused takes the separate-quantization route
+    (0 where the fused kernel is the faster)."""
+    return int(lib.mxq_gemm_w4a4_fused_workspace_bytes(M, N, K))
+
+
+def gemm_w4a4_fused(a, w_codes, w_scales, rule: str = "ocp", out=None, route: bool = True):
     """W4A4 with the activation quantization fused in: bf16 or fp32 A [M, K] (rows may be
-    strided) x MXFP4 W [N, K]^T -> bf16 [M, N]; equal to gemm_w4a4(*quantize(a, rule), W)."""
+    strided) x MXFP4 W [N, K]^T -> bf16 [M, N]; equal to gemm_w4a4(*quantize(a, rule), W).
+    route=True lends the call a workspace, so shapes past the fused kernel's break-even
+    quantize in a pass of their own; route=False always runs the fused kernel."""
     ld, dt = _input(a, "a")
     M, K = a.shape
     N = _mx_weights(w_codes, w_scales, K, a.device)
     out, ldo = _out(M, N, a.device, out)
+    nbytes = fused_workspace_bytes(M, N, K) if route else 0
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=a.device) if nbytes else None
     _check(lib.mxq_gemm_w4a4_fused(_p(a), dt, ld, _p(w_codes), _p(w_scales), M, N, K, _rule_code(rule),
-                                   _p(out), ldo, _stream()))
+                                   _p(out), ldo, _p(ws) if ws is not None else None, nbytes, _stream()))
     return out
 
 

@@ -205,9 +205,25 @@ mxq_status mxq_gemm_w4a4(const uint8_t* a_codes, const uint8_t* a_scales, const 
                                          out_bf16, ld_out, as_stream(stream)));
 }
 
+// Break-even of the fused W4A4 kernel: it quantizes every activation tile once per
+// 256-column output tile, so its cost grows with N, while quantization in a pass of its
+// own is paid once.  Measured on MI355X (M = 57344 and 75600): fused is the faster up to
+// 3 column tiles (N <= 768) for K >= 8192 (K = 12288: 0.99 of the separate pair at N = 768,
+// 1.05 at 1024; K = 13824: 0.96 and 1.02) and up to 1 tile for K = 3072 (0.96 at N = 256,
+// 1.04 at 512).
+int64_t fused_max_col_tiles(int64_t K) { return K >= 8192 ? 3 : 1; }
+int64_t round16(int64_t v) { return (v + 15) / 16 * 16; }
+
+size_t mxq_gemm_w4a4_fused_workspace_bytes(int64_t M, int64_t N, int64_t K) {
+  if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return 0;
+  if ((N + 255) / 256 <= fused_max_col_tiles(K)) return 0;
+  return (size_t)(round16(M * (K / 2)) + M * (K / 32));
+}
+
 mxq_status mxq_gemm_w4a4_fused(const void* a, mxq_dtype dt, int64_t ld_a, const uint8_t* w_codes,
                                const uint8_t* w_scales, int64_t M, int64_t N, int64_t K, mxq_scale_rule rule,
-                               uint16_t* out_bf16, int64_t ld_out, void* stream) {
+                               uint16_t* out_bf16, int64_t ld_out, void* workspace, size_t ws_bytes,
+                               void* stream) {
   const char* fn = "mxq_gemm_w4a4_fused";
   if (rule != MXQ_SCALE_OCP && rule != MXQ_SCALE_UOS)
     return fail(MXQ_ERR_UNSUPPORTED, "%s: unknown scale rule %d", fn, (int)rule);
@@ -222,6 +238,20 @@ mxq_status mxq_gemm_w4a4_fused(const void* a, mxq_dtype dt, int64_t ld_a, const 
     if ((st = check_operand(fn, "w_codes", w_codes, N, K, 16)) != MXQ_OK) return st;
     if ((st = check_operand(fn, "w_scales", w_scales, N, K, 1)) != MXQ_OK) return st;
     if (K > 0 && !a) return fail(MXQ_ERR_INVALID_ARG, "%s: a is NULL", fn);
+  }
+  const size_t need = mxq_gemm_w4a4_fused_workspace_bytes(M, N, K);
+  if (workspace && need > 0) {
+    // past the break-even: quantize into the workspace, then the W4A4 GEMM (the same bits)
+    if (!aligned(workspace, 16) || ws_bytes < need)
+      return fail(MXQ_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned and at least %zu bytes (got %zu)", fn,
+                  need, ws_bytes);
+    uint8_t* codes = static_cast<uint8_t*>(workspace);
+    uint8_t* scales = codes + round16(M * (K / 2));
+    hipError_t e = mxq::launch_quantize_mxfp4(a, dt == MXQ_F32, M, K, ld_a, codes, K / 2, scales, K / 32,
+                                              rule == MXQ_SCALE_UOS, as_stream(stream));
+    if (e != hipSuccess) return hip_status(fn, e);
+    return hip_status(fn, mxq::launch_gemm(mxq::GEMM_W4A4, codes, scales, w_codes, w_scales, 1.0f, M, N, K, out_bf16,
+                                           ld_out, as_stream(stream)));
   }
   return hip_status(fn, mxq::launch_gemm_w4a4_fused(a, dt == MXQ_F32, ld_a, w_codes, w_scales, M, N, K,
                                                     rule == MXQ_SCALE_UOS, out_bf16, ld_out, as_stream(stream)));

@@ -87,14 +87,19 @@ def _err():
     (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 48, 48, FAKE, 32, FAKE, 2, 1, None), "multiple of 32"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 96, 96, 64, 0, FAKE, 48, FAKE, 3, None), "multiple of block_n"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 0, FAKE, 16, FAKE, 2, None), "ld_codes"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 48, FAKE, FAKE, 8, 8, 48, 0, FAKE, 8, None), "multiple of 32"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 32, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "ld_x"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 68, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "aligned"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE_ODD, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "aligned"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 0, 1 << 21, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "row pitch"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, None, FAKE, 8, 8, 64, 0, FAKE, 8, None), "w_codes is NULL"),
-    (lambda L: L.mxq_gemm_w4a4_fused(None, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "NULL"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 4, None), "ld_out"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 48, FAKE, FAKE, 8, 8, 48, 0, FAKE, 8, None, 0, None), "multiple of 32"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 32, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "ld_x"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 68, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "aligned"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE_ODD, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "aligned"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 0, 1 << 21, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "row pitch"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, None, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "w_codes is NULL"),
+    (lambda L: L.mxq_gemm_w4a4_fused(None, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "NULL"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 4, None, 0, None), "ld_out"),
+    # past the fused kernel's break-even, a workspace that is too small or misaligned
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 8192, FAKE, FAKE, 8, 1024, 8192, 0, FAKE, 1024, FAKE, 16, None),
+     "workspace"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 8192, FAKE, FAKE, 8, 1024, 8192, 0, FAKE, 1024, FAKE_ODD, 1 << 20,
+                                     None), "workspace"),
     (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 8, 8, 48, 4, 1, FAKE, None), "multiple of 32"),
     (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 0, 8, 64, 4, 1, FAKE, None), "M, N >= 1"),
     (lambda L: L.mxq_mfma_ceiling(0, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, 6, 1, FAKE, None), "waves"),
@@ -119,8 +124,8 @@ def test_unknown_dtype_is_unsupported():
     (lambda L: L.mxq_quantize_rule(FAKE, 1, 4, 64, 64, FAKE, 32, FAKE, 2, 5, None), "scale rule"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 32, 0, FAKE, 32, FAKE, 2, None), "block_n"),
     (lambda L: L.mxq_quantize_hadamard(FAKE, 1, 4, 64, 64, 64, 3, FAKE, 32, FAKE, 2, None), "scale rule"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 2, FAKE, 8, None), "scale rule"),
-    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 9, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None), "dtype"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 1, 64, FAKE, FAKE, 8, 8, 64, 2, FAKE, 8, None, 0, None), "scale rule"),
+    (lambda L: L.mxq_gemm_w4a4_fused(FAKE, 9, 64, FAKE, FAKE, 8, 8, 64, 0, FAKE, 8, None, 0, None), "dtype"),
     (lambda L: L.mxq_mfma_ceiling(3, FAKE, FAKE, FAKE, FAKE, 8, 8, 64, 4, 1, FAKE, None), "mode"),
 ])
 def test_unknown_rule_or_block_is_unsupported(call, needle):
@@ -132,8 +137,21 @@ def test_empty_problems_are_noops():
     assert mxq.lib.mxq_quantize(None, 1, 0, 64, 64, None, 32, None, 2, None) == mxq.MXQ_OK
     assert mxq.lib.mxq_gemm_w4a4(None, None, None, None, 0, 8, 64, None, 8, None) == mxq.MXQ_OK
     assert mxq.lib.mxq_gemm_w4a8(None, ctypes.c_float(1.0), None, None, 8, 0, 64, None, 0, None) == mxq.MXQ_OK
-    assert mxq.lib.mxq_gemm_w4a4_fused(None, 1, 64, None, None, 0, 8, 64, 0, None, 8, None) == mxq.MXQ_OK
+    assert mxq.lib.mxq_gemm_w4a4_fused(None, 1, 64, None, None, 0, 8, 64, 0, None, 8, None, 0, None) == mxq.MXQ_OK
     assert _err() == ""
+
+
+@pytest.mark.parametrize("M,N,K,routes", [
+    (75600, 5120, 13824, True), (75600, 768, 13824, False), (75600, 769, 13824, True),
+    (57344, 12288, 3072, True), (57344, 256, 3072, False), (57344, 257, 3072, True),
+    (57344, 768, 8192, False), (57344, 1024, 8192, True), (0, 4096, 8192, False), (8, 4096, 48, False)])
+def test_fused_workspace_follows_the_break_even(M, N, K, routes):
+    n = mxq.lib.mxq_gemm_w4a4_fused_workspace_bytes(M, N, K)
+    assert mxq.fused_workspace_bytes(M, N, K) == n
+    if routes:
+        assert n == -(-(M * K // 2) // 16) * 16 + M * K // 32
+    else:
+        assert n == 0
 
 
 def test_workspace_size_is_fixed_and_small():

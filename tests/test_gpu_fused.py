@@ -13,7 +13,11 @@ therefore the oracle's chain (quantize_mxfp4, gemm_w4a4) within the GEMM bar.
   2 to 54 K-windows, row-strided activations and outputs, K off the fast path, binary32
   activations, both rules, the Wan2.2 FFN-down workload at reduced size and the Wan2.2
   FFN-down and FLUX FFN-up / FFN-down workloads at full size;
-* the oracle chain within the bar on the tiny workload (binary32) and sampled outputs.
+* the oracle chain within the bar on the tiny workload (binary32) and sampled outputs;
+* the call with a workspace, on both sides of the break-even where it routes to the
+  separate quantization pass: the same bits as the fused kernel and the chain.
+
+The tests of the fused kernel itself call it with route=False (no workspace).
 """
 
 import numpy as np
@@ -45,7 +49,7 @@ def _check_identity(mxq, a_gpu, a_host_f32, rule, label):
     for s_w in (191, 63):                      # x 2^64 and x 2^-64
         wc, wsc = _identity_weights(K, s_w)
         announce(f"fused identity {label} {rule} s_w={s_w} M={M} K={K} {a_gpu.dtype}")
-        out = mxq.gemm_w4a4_fused(a_gpu, wc, wsc, rule)
+        out = mxq.gemm_w4a4_fused(a_gpu, wc, wsc, rule, route=False)
         torch.cuda.synchronize()
         got = bf16_bits_to_f32(to_np_bf16_bits(out)).astype(np.float64)
         want = deq * 2.0 ** (s_w - 127)
@@ -114,7 +118,7 @@ def test_fused_bit_identical_to_quantize_then_gemm(gpu, M, N, K, rule):
     w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
     wc, wsc = gpu.quantize(w)
     announce(f"fused vs chain {rule} M={M} N={N} K={K}")
-    out = gpu.gemm_w4a4_fused(a, wc, wsc, rule)
+    out = gpu.gemm_w4a4_fused(a, wc, wsc, rule, route=False)
     ref = _chain(gpu, a, wc, wsc, rule)
     torch.cuda.synchronize()
     _assert_same(out, ref, f"{M}x{N}x{K} {rule}")
@@ -129,7 +133,7 @@ def test_fused_strided_activations_and_output(gpu):
     wc, wsc = gpu.quantize(w)
     out_full = torch.full((M, N + 8), 7.0, dtype=torch.bfloat16, device="cuda")
     announce("fused strided A and out")
-    gpu.gemm_w4a4_fused(a, wc, wsc, out=out_full[:, :N])
+    gpu.gemm_w4a4_fused(a, wc, wsc, out=out_full[:, :N], route=False)
     ref = _chain(gpu, a.contiguous(), wc, wsc, "ocp")
     torch.cuda.synchronize()
     _assert_same(out_full[:, :N], ref, "strided")
@@ -143,7 +147,7 @@ def test_fused_binary32_activations(gpu):
     w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
     wc, wsc = gpu.quantize(w)
     announce("fused binary32 activations")
-    out = gpu.gemm_w4a4_fused(a, wc, wsc)
+    out = gpu.gemm_w4a4_fused(a, wc, wsc, route=False)
     ref = _chain(gpu, a, wc, wsc, "ocp")
     torch.cuda.synchronize()
     _assert_same(out, ref, "binary32")
@@ -154,7 +158,7 @@ def test_fused_tiny_workload_against_oracle(gpu):
     ta, tw = torch.from_numpy(a).cuda(), torch.from_numpy(w).cuda()
     wc, wsc = gpu.quantize(tw)
     announce("fused tiny workload")
-    out = gpu.gemm_w4a4_fused(ta, wc, wsc)
+    out = gpu.gemm_w4a4_fused(ta, wc, wsc, route=False)
     torch.cuda.synchronize()
     rac, ras = oracle.quantize_mxfp4(a)
     rwc, rws = oracle.quantize_mxfp4(w)
@@ -169,7 +173,7 @@ def test_fused_workload_bitwise_and_oracle(gpu, name, M):
     a, w = workloads.workload_inputs(name, device="cuda", M=M)
     wc, wsc = gpu.quantize(w)
     announce(f"fused workload {name} {tuple(a.shape)}")
-    out = gpu.gemm_w4a4_fused(a, wc, wsc)
+    out = gpu.gemm_w4a4_fused(a, wc, wsc, route=False)
     ref = _chain(gpu, a, wc, wsc, "ocp")
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{name}: fused differs from the chain"
@@ -189,7 +193,32 @@ def test_fused_full_size_bitwise(gpu, name):
     a, w = workloads.workload_inputs(name, device="cuda")
     wc, wsc = gpu.quantize(w)
     announce(f"fused full size {name} {tuple(a.shape)}")
-    out = gpu.gemm_w4a4_fused(a, wc, wsc)
+    out = gpu.gemm_w4a4_fused(a, wc, wsc, route=False)
     ref = _chain(gpu, a, wc, wsc, "ocp")
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), f"{name}: full-size fused output differs from the chain"
+    # past the break-even the call with a workspace quantizes in a pass of its own
+    assert gpu.fused_workspace_bytes(*a.shape[:1], w.shape[0], a.shape[1]) > 0
+    routed = gpu.gemm_w4a4_fused(a, wc, wsc)
+    torch.cuda.synchronize()
+    assert torch.equal(routed.view(torch.int16), ref.view(torch.int16)), f"{name}: routed call differs from the chain"
+
+
+@pytest.mark.parametrize("M,N,K", [(300, 256, 3072), (300, 520, 3072), (200, 768, 8192), (200, 1030, 8192),
+                                   (97, 900, 8224)])
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_routed_call_equals_fused_kernel(gpu, M, N, K, rule):
+    g = torch.Generator(device="cuda").manual_seed(M + N + K)
+    a = (torch.randn(M, K, device="cuda", generator=g) * torch.exp(torch.randn(1, K, device="cuda", generator=g)))
+    a = a.to(torch.bfloat16)
+    w = (torch.randn(N, K, device="cuda", generator=g) * 0.02).to(torch.bfloat16)
+    wc, wsc = gpu.quantize(w)
+    routes = gpu.fused_workspace_bytes(M, N, K) > 0
+    assert routes == ((N + 255) // 256 > (3 if K >= 8192 else 1))
+    announce(f"routed vs fused {rule} M={M} N={N} K={K} routes={routes}")
+    fused = gpu.gemm_w4a4_fused(a, wc, wsc, rule, route=False)
+    routed = gpu.gemm_w4a4_fused(a, wc, wsc, rule)
+    ref = _chain(gpu, a, wc, wsc, rule)
+    torch.cuda.synchronize()
+    _assert_same(routed, fused, f"routed {M}x{N}x{K} {rule}")
+    _assert_same(routed, ref, f"chain {M}x{N}x{K} {rule}")

@@ -57,7 +57,7 @@ class _Step:
         m.gemm_bf16(self.a, self.w, out=self.ref)
         m.sqnr(self.ref, self.o44, workspace=self.ws1, out3=self.r44)
         m.sqnr(self.ref, self.o48, workspace=self.ws2, out3=self.r48)
-        m.gemm_w4a4_fused(self.a, self.wc, self.wsc, out=self.of)
+        m.gemm_w4a4_fused(self.a, self.wc, self.wsc, out=self.of, route=False)
 
     def outputs(self):
         return [t.clone() for t in (self.ac, self.asc, self.a8, self.o44, self.o48, self.ref, self.of,
