@@ -37,13 +37,14 @@ constexpr int kMxUnroll = 8;
 constexpr int kMxBlocksPerIter = kMxThreads / 4 * kMxUnroll;
 constexpr int kFp8Threads = 1024;
 constexpr int kFp8Unroll = 2;     // chunks of 16 per lane per pass (72 % of HBM against 69 % for one)
-// dequantize_kernel: 8 quarter-blocks per lane per pass in 512-thread workgroups (71 % of
-// HBM against 58 % for one quarter per lane and 256 threads)
-constexpr int kDqThreads = 512;
-constexpr int kDqUnroll = 8;
+// dequantize_kernel: 4 quarter-blocks per lane per pass in 1024-thread workgroups, loads
+// first (72 % of HBM; 512 threads with 2, 8 or 16 quarters and 256 threads with 8 within
+// 4 % of it; 58 % for one quarter per lane and 256 threads)
+constexpr int kDqThreads = 1024;
+constexpr int kDqUnroll = 4;
 // dequantize_fp8_kernel: 8 codes (8 bytes in, 16 bytes out) per lane per unit, 4 units
-// per lane per pass, loads first
-constexpr int kDq8Threads = 512;
+// per lane per pass, loads first, 1024-thread workgroups (the same sweep: within 4 %)
+constexpr int kDq8Threads = 1024;
 constexpr int kDq8Unroll = 4;
 // mx_quantize_rot_kernel: 512-thread workgroups, 4 blocks in flight per quad, every load
 // of an iteration issued before its butterflies (66 % of HBM for n = 64 against 61 % with
@@ -188,8 +189,15 @@ __global__ __launch_bounds__(THREADS) void mx_quantize_rot_kernel(
   constexpr float kNorm = N == 16 ? 0.25f : (N == 64 ? 0.125f : 0.0625f);   // 1 / sqrt(N)
   constexpr int BLOCKS_PER_ITER = THREADS / 4 * UNROLL;
   const int tid = threadIdx.x;
-  const int q = tid & 3;
+  // Lanes are relabelled inside each group of 8 for n >= 64: lane p holds the data of
+  // logical lane l = p ^ 3 * bit2(p), an involution that keeps every quad (block) together
+  // and turns the logical exchange at distance 4 into p ^ 7, the half-row mirror of DPP,
+  // one operand modifier instead of two shifts and a select.  Distances 1, 2, 8 and 16
+  // map to themselves.
+  constexpr bool RELABEL = N >= 64;
   const int lane = tid & 63;
+  const int llane = RELABEL ? lane ^ (((lane >> 2) & 1) * 3) : lane;
+  const int q = llane & 3;                     // quarter of the block this lane owns
   const int64_t stride = (int64_t)gridDim.x * BLOCKS_PER_ITER;
   for (int64_t base = (int64_t)blockIdx.x * BLOCKS_PER_ITER; base < total_blocks; base += stride) {
     // every block's loads first, then the butterflies and stores
@@ -198,7 +206,7 @@ __global__ __launch_bounds__(THREADS) void mx_quantize_rot_kernel(
     v4i d0[UNROLL], d1[UNROLL];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      const int64_t b = base + u * (THREADS / 4) + (tid >> 2);
+      const int64_t b = base + u * (THREADS / 4) + (tid >> 2);   // a quad's block: relabelling stays in the quad
       ok[u] = b < total_blocks;
       int64_t xo;
       if (contiguous) {
@@ -225,76 +233,90 @@ __global__ __launch_bounds__(THREADS) void mx_quantize_rot_kernel(
         }
       }
     }
+    // Every stage runs over all UNROLL blocks before the next one, so a DPP read of a value
+    // sits a whole stage after the add that wrote it (no hazard wait states).
+    float v[UNROLL][8];
 #pragma unroll
     for (int u = 0; u < UNROLL; ++u) {
-      float v[8];
       if (F32) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[i] = __int_as_float(d0[u][i]);
-          v[4 + i] = __int_as_float(d1[u][i]);
+          v[u][i] = __int_as_float(d0[u][i]);
+          v[u][4 + i] = __int_as_float(d1[u][i]);
         }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          v[2 * i] = lo_f32(d0[u][i]);
-          v[2 * i + 1] = hi_f32(d0[u][i]);
+          v[u][2 * i] = lo_f32(d0[u][i]);
+          v[u][2 * i + 1] = hi_f32(d0[u][i]);
         }
       }
-      // stages h = 1, 2, 4 inside the lane
+    }
+    // stages h = 1, 2, 4 inside the lane
 #pragma unroll
-      for (int h = 1; h < 8; h *= 2)
+    for (int h = 1; h < 8; h *= 2)
+#pragma unroll
+      for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
           if ((i & h) == 0) {
-            const float a = v[i], c = v[i + h];
-            v[i] = __fadd_rn(a, c);
-            v[i + h] = __fsub_rn(a, c);
+            const float a = v[u][i], c = v[u][i + h];
+            v[u][i] = __fadd_rn(a, c);
+            v[u][i + h] = __fsub_rn(a, c);
           }
-      // Stages h = 8, 16, ... across lanes l and l ^ (h / 8); the lower index keeps the sum.
-      // Both lanes form partner + own', own' = own with its sign flipped in the upper lane:
-      // x_i + x_{i+h} (addition commutes) and x_i + (-x_{i+h}), the same binary32 operation
-      // as x_i - x_{i+h}.  One add per element and stage, the exchange folded into it as a
-      // DPP operand where one DPP pattern reaches the partner.
-      auto cross = [&](auto d_tag) {
-        constexpr int D = decltype(d_tag)::value;
-        if constexpr (D < N / 8) {
-          const unsigned flip = (lane & D) ? 0x80000000u : 0u;
+    // Stages h = 8, 16, ... across lanes l and l ^ (h / 8); the lower index keeps the sum.
+    // Both lanes form partner + own', own' = own with its sign flipped in the upper lane:
+    // x_i + x_{i+h} (addition commutes) and x_i + (-x_{i+h}), the same binary32 operation
+    // as x_i - x_{i+h}.  One add per element and stage, the exchange folded into it as a
+    // DPP operand.
+    auto cross = [&](auto d_tag) {
+      constexpr int D = decltype(d_tag)::value;
+      if constexpr (D < N / 8) {
+        const unsigned flip = (llane & D) ? 0x80000000u : 0u;
+        // all sign flips of the stage first: a DPP add waits out two cycles after any
+        // write of either of its operands
+        float own[UNROLL][8];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) own[u][i] = __uint_as_float(__float_as_uint(v[u][i]) ^ flip);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
-            const float own = __uint_as_float(__float_as_uint(v[i]) ^ flip);
-            if constexpr (D == 4) {
-              // lane + 4 for the lower half of each 8 lanes, lane - 4 for the upper half
-              const int b = __float_as_int(v[i]);
-              const float lo = __fadd_rn(__int_as_float(__builtin_amdgcn_mov_dpp(b, 0x104, 0xF, 0xF, true)), own);
-              const float hi = __fadd_rn(__int_as_float(__builtin_amdgcn_mov_dpp(b, 0x114, 0xF, 0xF, true)), own);
-              v[i] = (lane & 4) ? hi : lo;
-            } else {
-              v[i] = __fadd_rn(lane_xor<D>(v[i], lane), own);
-            }
+            float partner;
+            if constexpr (D == 4 && RELABEL)   // logical lane ^ 4 is physical lane ^ 7
+              partner = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[u][i]), 0x141, 0xF, 0xF, true));
+            else
+              partner = lane_xor<D>(v[u][i], lane);
+            v[u][i] = __fadd_rn(partner, own[u][i]);
           }
-        }
-      };
-      cross(std::integral_constant<int, 1>{});
-      cross(std::integral_constant<int, 2>{});
-      cross(std::integral_constant<int, 4>{});
-      cross(std::integral_constant<int, 8>{});
-      cross(std::integral_constant<int, 16>{});
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    cross(std::integral_constant<int, 1>{});
+    cross(std::integral_constant<int, 2>{});
+    cross(std::integral_constant<int, 4>{});
+    cross(std::integral_constant<int, 8>{});
+    cross(std::integral_constant<int, 16>{});
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[i] = __fmul_rn(v[i], kNorm);
+    for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[u][i] = __fmul_rn(v[u][i], kNorm);
       // MXFP4 of the rotated binary32 values (as mx_quantize_kernel)
       unsigned m = 0;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[i]) & 0x7FFFFFFFu);
+      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
       const unsigned amax = quad_max_u32(m);
       const unsigned e = amax >> 23;
       const unsigned s = UOS ? scale_byte_uos(e, (amax & 0x7FFFFFu) > 0x680000u ? 1u : 0u) : scale_byte_from_exp(e);
       const float scale = e8m0_to_f32(s);
       unsigned r = 0;
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[0], v[1], scale, 0);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[2], v[3], scale, 1);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4], v[5], scale, 2);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[6], v[7], scale, 3);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][0], v[u][1], scale, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][2], v[u][3], scale, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][4], v[u][5], scale, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][6], v[u][7], scale, 3);
       if (ok[u]) {
         __builtin_nontemporal_store(r, reinterpret_cast<unsigned*>(codes + co[u]));
         if (q == 0) scales[so[u]] = (uint8_t)s;
