@@ -35,6 +35,8 @@
  *    launched: an error return means nothing was enqueued.  MXQ_ERR_HIP reports a HIP
  *    launch error (e.g. no device present).
  *  - Empty problems (rows == 0, M == 0 or N == 0) are valid and enqueue nothing.
+ *  - Sizes: dimensions below 2^31, row pitches (ld_*) below 2^32 elements, so every
+ *    offset the library forms fits in int64; larger values are MXQ_ERR_INVALID_ARG.
  *  - Layouts (all row-major):
  *      MXFP4 codes  : uint8 [rows x ld_codes], byte j of a row holds element 2j in the
  *                     low nibble and element 2j+1 in the high nibble; an E2M1 code is
@@ -45,7 +47,8 @@
  *      bf16         : uint16 bit patterns.
  *    The quantizer's output is exactly the GEMMs' input: there is no hidden reshuffle.
  *    GEMM weights W are N x K with K contiguous (nn.Linear layout); out = A * W^T.
- *  - Thread safety: no global mutable state except the thread-local error message.
+ *  - Thread safety: no global mutable state except the thread-local error message and
+ *    the per-GPU scratch of mxq_sqnr_noalloc (calls of it that overlap on one GPU race).
  */
 #ifndef MXQ_H
 #define MXQ_H
@@ -57,16 +60,20 @@
 extern "C" {
 #endif
 
-#define MXQ_ABI_VERSION 1
+/* 2: mxq_gemm_w4a4_fused takes a workspace; mxq_gemm_w4a4_fused_workspace_bytes */
+#define MXQ_ABI_VERSION 2
 
 typedef enum {
   MXQ_OK = 0,
   MXQ_ERR_INVALID_ARG = 1, /* bad size, pointer, alignment or leading dimension */
   MXQ_ERR_UNSUPPORTED = 2, /* well-formed request the library does not serve (e.g. unknown dtype) */
-  MXQ_ERR_HIP = 3          /* a HIP runtime call or kernel launch failed */
+  MXQ_ERR_HIP = 3,         /* a HIP runtime call or kernel launch failed */
+  MXQ_STATUS_MAX_ENUM = 0x7FFFFFFF
 } mxq_status;
 
-typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1 } mxq_dtype;
+/* Every enum ends in a *_MAX_ENUM member so that it spans all int32 values: an unknown
+ * value passed in is then a defined value the library rejects (MXQ_ERR_UNSUPPORTED). */
+typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1, MXQ_DTYPE_MAX_ENUM = 0x7FFFFFFF } mxq_dtype;
 
 /*
  * mxq_quantize -- MXFP4 block quantization along each row ([FLX] "What is MXFP4";
@@ -89,7 +96,8 @@ mxq_status mxq_quantize(const void* x, mxq_dtype dt, int64_t rows, int64_t cols,
 /* Scale rule of mxq_quantize_rule. */
 typedef enum {
   MXQ_SCALE_OCP = 0, /* X = 2^(floor(log2 amax) - 2): the rule of mxq_quantize */
-  MXQ_SCALE_UOS = 1  /* X = smallest power of two with amax <= 7.25 X */
+  MXQ_SCALE_UOS = 1, /* X = smallest power of two with amax <= 7.25 X */
+  MXQ_SCALE_RULE_MAX_ENUM = 0x7FFFFFFF
 } mxq_scale_rule;
 
 /*
@@ -316,7 +324,12 @@ mxq_status mxq_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int
  * Errors : MXQ_ERR_UNSUPPORTED for an unknown mode, MXQ_ERR_INVALID_ARG for bad sizes or
  *          pointers, checked before anything is enqueued.
  */
-typedef enum { MXQ_GEMM_W4A4 = 0, MXQ_GEMM_W4A8 = 1, MXQ_GEMM_BF16 = 2 } mxq_gemm_mode;
+typedef enum {
+  MXQ_GEMM_W4A4 = 0,
+  MXQ_GEMM_W4A8 = 1,
+  MXQ_GEMM_BF16 = 2,
+  MXQ_GEMM_MODE_MAX_ENUM = 0x7FFFFFFF
+} mxq_gemm_mode;
 mxq_status mxq_mfma_ceiling(mxq_gemm_mode mode, const void* a, const uint8_t* a_scales,
                             const void* w, const uint8_t* w_scales, int64_t M, int64_t N,
                             int64_t K, int64_t waves, int64_t iters, float* sink, void* stream);

@@ -37,12 +37,18 @@ mxq_status hip_status(const char* fn, hipError_t e) {
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Row pitches (elements or bytes) are below 2^32, dimensions below 2^31: every product the
+// checks and the launchers form then stays inside int64.
+constexpr int64_t kMaxPitch = ((int64_t)1 << 32) - 1;
+constexpr int64_t kMaxDim = 0x7FFFFFFF;
+bool pitch_ok(int64_t ld) { return ld <= kMaxPitch; }
+
 int dtype_bytes(mxq_dtype dt) {
   switch (dt) {
     case MXQ_F32: return 4;
     case MXQ_BF16: return 2;
+    default: return 0;   // unknown: rejected by the callers
   }
-  return 0;
 }
 
 // Shared checks for a rows x cols input of dtype dt with pitch ld (elements).
@@ -54,13 +60,13 @@ mxq_status check_input(const char* fn, const void* x, mxq_dtype dt, int64_t rows
     return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of %lld", fn, (long long)cols,
                 (long long)col_multiple);
   if (ld < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_x (%lld) < cols (%lld)", fn, (long long)ld, (long long)cols);
+  if (rows > kMaxDim || cols > kMaxDim) return fail(MXQ_ERR_INVALID_ARG, "%s: dimension exceeds 2^31-1", fn);
+  if (!pitch_ok(ld)) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_x (%lld) must be below 2^32", fn, (long long)ld);
   if (rows > 0 && cols > 0) {
     if (!x) return fail(MXQ_ERR_INVALID_ARG, "%s: x is NULL", fn);
     if (!aligned(x, 16) || (ld * dtype_bytes(dt)) % 16 != 0)
       return fail(MXQ_ERR_INVALID_ARG, "%s: x base and row pitch must be 16-byte aligned", fn);
   }
-  if (rows > (int64_t)0x7FFFFFFF || cols > (int64_t)0x7FFFFFFF)
-    return fail(MXQ_ERR_INVALID_ARG, "%s: dimension exceeds 2^31-1", fn);
   if ((rows * (cols / 8 > 0 ? cols / 8 : 1)) >= ((int64_t)1 << 32))
     return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large (more than 2^35 elements)", fn);
   return MXQ_OK;
@@ -74,6 +80,7 @@ mxq_status check_gemm(const char* fn, int64_t M, int64_t N, int64_t K, const voi
   if (M > (int64_t)0x7FFFFFFF - 256 || N > (int64_t)0x7FFFFFFF - 256 || K > ((int64_t)1 << 21))
     return fail(MXQ_ERR_INVALID_ARG, "%s: dimension too large", fn);
   if (ld_out < N) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_out (%lld) < N (%lld)", fn, (long long)ld_out, (long long)N);
+  if (!pitch_ok(ld_out)) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_out (%lld) must be below 2^32", fn, (long long)ld_out);
   if (M > 0 && N > 0) {
     if (!out) return fail(MXQ_ERR_INVALID_ARG, "%s: out is NULL", fn);
     if (!aligned(out, 2)) return fail(MXQ_ERR_INVALID_ARG, "%s: out must be 2-byte aligned", fn);
@@ -110,6 +117,7 @@ mxq_status mxq_quantize_rule(const void* x, mxq_dtype dt, int64_t rows, int64_t 
   if (st != MXQ_OK) return st;
   if (ld_codes < cols / 2) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_codes (%lld) < cols/2", fn, (long long)ld_codes);
   if (ld_scales < cols / 32) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_scales (%lld) < cols/32", fn, (long long)ld_scales);
+  if (!pitch_ok(ld_codes) || !pitch_ok(ld_scales)) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch must be below 2^32", fn);
   if (rows > 0 && cols > 0) {
     if (!codes || !scales) return fail(MXQ_ERR_INVALID_ARG, "%s: codes/scales is NULL", fn);
     if (!aligned(codes, 16) || ld_codes % 16 != 0)
@@ -138,6 +146,7 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int6
     return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of block_n (%d)", fn, (long long)cols, block_n);
   if (ld_codes < cols / 2) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_codes (%lld) < cols/2", fn, (long long)ld_codes);
   if (ld_scales < cols / 32) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_scales (%lld) < cols/32", fn, (long long)ld_scales);
+  if (!pitch_ok(ld_codes) || !pitch_ok(ld_scales)) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch must be below 2^32", fn);
   if (rows > 0 && cols > 0) {
     if (!codes || !scales) return fail(MXQ_ERR_INVALID_ARG, "%s: codes/scales is NULL", fn);
     if (!aligned(codes, 16) || ld_codes % 16 != 0)
@@ -155,6 +164,7 @@ mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t c
   if (!(inv_scale > 0.0f) || !(inv_scale < __builtin_inff()))
     return fail(MXQ_ERR_INVALID_ARG, "%s: inv_scale must be finite and > 0", fn);
   if (ld_q < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_q (%lld) < cols", fn, (long long)ld_q);
+  if (!pitch_ok(ld_q)) return fail(MXQ_ERR_INVALID_ARG, "%s: ld_q (%lld) must be below 2^32", fn, (long long)ld_q);
   if (rows > 0 && cols > 0) {
     if (!q) return fail(MXQ_ERR_INVALID_ARG, "%s: q is NULL", fn);
     if (!aligned(q, 16) || ld_q % 16 != 0)
@@ -216,6 +226,7 @@ int64_t round16(int64_t v) { return (v + 15) / 16 * 16; }
 
 size_t mxq_gemm_w4a4_fused_workspace_bytes(int64_t M, int64_t N, int64_t K) {
   if (M <= 0 || N <= 0 || K <= 0 || K % 32 != 0) return 0;
+  if (M > kMaxDim || N > kMaxDim || K > ((int64_t)1 << 21)) return 0;   // a shape the GEMM rejects
   if ((N + 255) / 256 <= fused_max_col_tiles(K)) return 0;
   return (size_t)(round16(M * (K / 2)) + M * (K / 32));
 }
@@ -295,7 +306,8 @@ mxq_status mxq_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, int
   if (cols % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
   if (ld_ref < cols || ld_test < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below cols", fn);
   if (ld_ref % 8 != 0 || ld_test % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: pitches must be multiples of 8", fn);
-  if (rows > (int64_t)0x7FFFFFFF || cols > (int64_t)0x7FFFFFFF || rows * (cols / 8) >= ((int64_t)1 << 32))
+  if (rows > kMaxDim || cols > kMaxDim || !pitch_ok(ld_ref) || !pitch_ok(ld_test) ||
+      rows * (cols / 8) >= ((int64_t)1 << 32))
     return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
   if (!out3 || !aligned(out3, 8)) return fail(MXQ_ERR_INVALID_ARG, "%s: out3 must be a non-NULL 8-byte aligned pointer", fn);
   if (!workspace || !aligned(workspace, 8) || ws_bytes < mxq::sqnr_workspace_bytes(rows * cols))
@@ -315,7 +327,8 @@ mxq_status mxq_sqnr_noalloc(const uint16_t* ref, const uint16_t* test, int64_t r
   if (cols % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 8", fn, (long long)cols);
   if (ld_ref < cols || ld_test < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below cols", fn);
   if (ld_ref % 8 != 0 || ld_test % 8 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: pitches must be multiples of 8", fn);
-  if (rows > (int64_t)0x7FFFFFFF || cols > (int64_t)0x7FFFFFFF || rows * (cols / 8) >= ((int64_t)1 << 32))
+  if (rows > kMaxDim || cols > kMaxDim || !pitch_ok(ld_ref) || !pitch_ok(ld_test) ||
+      rows * (cols / 8) >= ((int64_t)1 << 32))
     return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
   const size_t need = mxq::sqnr_workspace_bytes(rows * cols);
   if (need > mxq::sqnr_scratch_bytes())
@@ -339,7 +352,8 @@ mxq_status mxq_dequantize(const uint8_t* codes, int64_t ld_codes, const uint8_t*
   if (cols % 32 != 0) return fail(MXQ_ERR_INVALID_ARG, "%s: cols (%lld) must be a multiple of 32", fn, (long long)cols);
   if (ld_codes < cols / 2 || ld_scales < cols / 32 || ld_y < cols)
     return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below the row width", fn);
-  if (rows > (int64_t)0x7FFFFFFF || rows * (cols / 32) >= ((int64_t)1 << 30))
+  if (rows > kMaxDim || cols > kMaxDim || !pitch_ok(ld_codes) || !pitch_ok(ld_scales) || !pitch_ok(ld_y) ||
+      rows * (cols / 32) >= ((int64_t)1 << 30))
     return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
   if (rows > 0 && cols > 0) {
     if (!codes || !scales || !y) return fail(MXQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);
@@ -358,7 +372,7 @@ mxq_status mxq_dequantize_fp8(const uint8_t* q, int64_t ld_q, float a_scale, int
   if (ld_q < cols || ld_y < cols) return fail(MXQ_ERR_INVALID_ARG, "%s: pitch below the row width", fn);
   if (!(a_scale == a_scale) || a_scale == __builtin_inff() || a_scale == -__builtin_inff())
     return fail(MXQ_ERR_INVALID_ARG, "%s: a_scale must be finite", fn);
-  if (rows > (int64_t)0x7FFFFFFF || rows * (cols / 8) >= ((int64_t)1 << 32))
+  if (rows > kMaxDim || cols > kMaxDim || !pitch_ok(ld_q) || !pitch_ok(ld_y) || rows * (cols / 8) >= ((int64_t)1 << 32))
     return fail(MXQ_ERR_INVALID_ARG, "%s: tensor too large", fn);
   if (rows > 0 && cols > 0) {
     if (!q || !y) return fail(MXQ_ERR_INVALID_ARG, "%s: NULL pointer", fn);

@@ -41,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert mxq.lib.mxq_abi_version() == 1
+    assert mxq.lib.mxq_abi_version() == 2
 
 
 def _err():
