@@ -19,9 +19,9 @@ CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmxq.so")
 ARCH = "gfx950"
 
-SOURCES = ["mxq_api.hip", "quantize.hip", "gemm.hip", "gemm_scaled.hip", "sqnr.hip", "ceiling.hip"]
-# per-source compiler options (gemm_scaled.hip: see the comment at its top)
-SOURCE_FLAGS = {"gemm_scaled.hip": ["-mllvm", "-disable-machine-sink"]}
+SOURCES = ["mxq_api.hip", "quantize.hip", "hadamard.hip", "gemm.hip", "gemm_scaled.hip", "sqnr.hip", "ceiling.hip"]
+# per-source compiler options (see the comment at the top of each source)
+SOURCE_FLAGS = {"gemm_scaled.hip": ["-mllvm", "-disable-machine-sink"], "hadamard.hip": ["-fno-slp-vectorize"]}
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",

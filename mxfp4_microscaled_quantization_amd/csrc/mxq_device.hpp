@@ -10,6 +10,7 @@ namespace mxq {
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef unsigned v2u __attribute__((ext_vector_type(2)));
+typedef unsigned v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned short v2h __attribute__((ext_vector_type(2)));
@@ -29,6 +30,11 @@ __device__ __forceinline__ unsigned quad_max_u32(unsigned v) {
   v = max(v, (unsigned)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));  // lane ^ 2
   return v;
 }
+
+// The low / high bf16 of a packed pair as binary32 (exact: the bf16 bits become the top
+// half of the binary32 word).
+__device__ __forceinline__ float bf16_lo_f32(int pair) { return __uint_as_float((unsigned)pair << 16); }
+__device__ __forceinline__ float bf16_hi_f32(int pair) { return __uint_as_float((unsigned)pair & 0xFFFF0000u); }
 
 // Two floats -> packed bf16x2 (round to nearest even; v_cvt_pk_bf16_f32).
 __device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {

@@ -21,8 +21,6 @@
 // gfx950 conversion v_cvt_scalef32_pk_fp4_f32, which computes round-to-nearest-even of
 // x / scale with saturation for power-of-two scales (including the subnormal 2^-127), two
 // elements per instruction (bf16 inputs are widened exactly first).
-#include <type_traits>
-
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -46,14 +44,6 @@ constexpr int kDqUnroll = 4;
 // per lane per pass, loads first, 1024-thread workgroups (the same sweep: within 4 %)
 constexpr int kDq8Threads = 1024;
 constexpr int kDq8Unroll = 4;
-// mx_quantize_rot_kernel: 512-thread workgroups, 4 blocks in flight per quad, every load
-// of an iteration issued before its butterflies (66 % of HBM for n = 64 against 61 % with
-// 256 threads and each block's load, butterfly and store in turn)
-constexpr int kRotThreads = 512;
-constexpr int kRotUnroll = 4;
-
-__device__ __forceinline__ float lo_f32(int pair) { return __uint_as_float((unsigned)pair << 16); }
-__device__ __forceinline__ float hi_f32(int pair) { return __uint_as_float((unsigned)pair & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------------
 // MXFP4 quantization.  F32 selects binary32 input (else bf16); UOS the 7.25 boundary.
@@ -131,193 +121,13 @@ __global__ __launch_bounds__(kMxThreads) void mx_quantize_kernel(
       } else {
         // bf16 pairs are widened exactly to binary32 (a shift / a mask) and converted
         // with the f32 form, whose destination-byte select places byte k of the word
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][0]), hi_f32(d0[u][0]), scale, 0);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][1]), hi_f32(d0[u][1]), scale, 1);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][2]), hi_f32(d0[u][2]), scale, 2);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, lo_f32(d0[u][3]), hi_f32(d0[u][3]), scale, 3);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][0]), bf16_hi_f32(d0[u][0]), scale, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][1]), bf16_hi_f32(d0[u][1]), scale, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][2]), bf16_hi_f32(d0[u][2]), scale, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][3]), bf16_hi_f32(d0[u][3]), scale, 3);
       }
       if (ok[u]) {
         // codes are not read again by this kernel: stream them past the caches
-        __builtin_nontemporal_store(r, reinterpret_cast<unsigned*>(codes + co[u]));
-        if (q == 0) scales[so[u]] = (uint8_t)s;
-      }
-    }
-  }
-}
-
-// ---------------------------------------------------------------------------------
-// Fixed block-Hadamard rotation, then MXFP4 ("AMD Quark adds native W4A8 mixed-precision
-// for Wan2.2 ...", section "Quark quantization pipeline and mixed-precision selection":
-// a fixed Hadamard rotation as the transform condition; "Exp 2026-08-22 W4A4 Reference
-// Model", section "Status": block-Hadamard with per-group scales).  Every run of N
-// consecutive elements along K becomes x H_N / sqrt(N) (Sylvester H_N, N = 16, 64, 256,
-// so 1/sqrt(N) is a power of two), formed in binary32 by the radix-2 butterfly in stage
-// order h = 1, 2, 4, ...: the pair (i, i + h) becomes (x_i + x_{i+h}, x_i - x_{i+h}).
-// The rotated values are then quantized as binary32 input.  Same lane mapping as
-// mx_quantize_kernel (4 lanes per 32-element block, 8 elements per lane): stages h < 8
-// stay in the lane, stages h >= 8 pair lane l with lane l ^ (h / 8).  A run never straddles
-// a row (K % N == 0) and starts at a multiple of N / 8 lanes.  Adds and the final scaling
-// are explicitly rounded (no contraction into fused operations).
-// value of lane l ^ D (D < 32): DPP inside a row of 16 lanes (quad permutes for 1 and 2,
-// row shifts for 4, a row rotation for 8), a permute through the LDS crossbar beyond
-template <int D>
-__device__ __forceinline__ float lane_xor(float v, int lane) {
-  const int b = __float_as_int(v);
-  if constexpr (D == 1) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0xB1, 0xF, 0xF, true));    // quad_perm [1,0,3,2]
-  } else if constexpr (D == 2) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x4E, 0xF, 0xF, true));    // quad_perm [2,3,0,1]
-  } else if constexpr (D == 4) {
-    const int up = __builtin_amdgcn_mov_dpp(b, 0x104, 0xF, 0xF, true);          // row_shl:4 (lane + 4)
-    const int dn = __builtin_amdgcn_mov_dpp(b, 0x114, 0xF, 0xF, true);          // row_shr:4 (lane - 4)
-    return __int_as_float((lane & 4) ? dn : up);
-  } else if constexpr (D == 8) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(b, 0x128, 0xF, 0xF, true));   // row_ror:8
-  } else {
-    // through the LDS crossbar (ds_bpermute): measured faster here than the gfx950
-    // v_permlane16_swap, whose operand copies and hazard waits serialize the exchanges
-    return __shfl_xor(v, D);
-  }
-}
-
-template <bool F32, int N, bool UOS, int THREADS, int UNROLL>
-__global__ __launch_bounds__(THREADS) void mx_quantize_rot_kernel(
-    const void* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ codes, int64_t ld_codes,
-    uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks,
-    int contiguous) {
-  static_assert(N == 16 || N == 64 || N == 256, "rotation runs of 16, 64 or 256");
-  constexpr float kNorm = N == 16 ? 0.25f : (N == 64 ? 0.125f : 0.0625f);   // 1 / sqrt(N)
-  constexpr int BLOCKS_PER_ITER = THREADS / 4 * UNROLL;
-  const int tid = threadIdx.x;
-  // Lanes are relabelled inside each group of 8 for n >= 64: lane p holds the data of
-  // logical lane l = p ^ 3 * bit2(p), an involution that keeps every quad (block) together
-  // and turns the logical exchange at distance 4 into p ^ 7, the half-row mirror of DPP,
-  // one operand modifier instead of two shifts and a select.  Distances 1, 2, 8 and 16
-  // map to themselves.
-  constexpr bool RELABEL = N >= 64;
-  const int lane = tid & 63;
-  const int llane = RELABEL ? lane ^ (((lane >> 2) & 1) * 3) : lane;
-  const int q = llane & 3;                     // quarter of the block this lane owns
-  const int64_t stride = (int64_t)gridDim.x * BLOCKS_PER_ITER;
-  for (int64_t base = (int64_t)blockIdx.x * BLOCKS_PER_ITER; base < total_blocks; base += stride) {
-    // every block's loads first, then the butterflies and stores
-    int64_t co[UNROLL], so[UNROLL];
-    bool ok[UNROLL];
-    v4i d0[UNROLL], d1[UNROLL];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      const int64_t b = base + u * (THREADS / 4) + (tid >> 2);   // a quad's block: relabelling stays in the quad
-      ok[u] = b < total_blocks;
-      int64_t xo;
-      if (contiguous) {
-        xo = b * 32 + q * 8;
-        co[u] = b * 16 + q * 4;
-        so[u] = b;
-      } else {
-        const uint32_t bb = (uint32_t)b;
-        const uint32_t row = bb / blocks_per_row;
-        const uint32_t blk = bb - row * blocks_per_row;
-        xo = (int64_t)row * ld_x + blk * 32 + q * 8;
-        co[u] = (int64_t)row * ld_codes + blk * 16 + q * 4;
-        so[u] = (int64_t)row * ld_scales + blk;
-      }
-      d0[u] = v4i{0, 0, 0, 0};
-      d1[u] = v4i{0, 0, 0, 0};
-      if (ok[u]) {
-        if (F32) {
-          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
-          d0[u] = __builtin_nontemporal_load(p);
-          d1[u] = __builtin_nontemporal_load(p + 1);
-        } else {
-          d0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo));
-        }
-      }
-    }
-    // Every stage runs over all UNROLL blocks before the next one, so a DPP read of a value
-    // sits a whole stage after the add that wrote it (no hazard wait states).
-    float v[UNROLL][8];
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-      if (F32) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[u][i] = __int_as_float(d0[u][i]);
-          v[u][4 + i] = __int_as_float(d1[u][i]);
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          v[u][2 * i] = lo_f32(d0[u][i]);
-          v[u][2 * i + 1] = hi_f32(d0[u][i]);
-        }
-      }
-    }
-    // stages h = 1, 2, 4 inside the lane
-#pragma unroll
-    for (int h = 1; h < 8; h *= 2)
-#pragma unroll
-      for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          if ((i & h) == 0) {
-            const float a = v[u][i], c = v[u][i + h];
-            v[u][i] = __fadd_rn(a, c);
-            v[u][i + h] = __fsub_rn(a, c);
-          }
-    // Stages h = 8, 16, ... across lanes l and l ^ (h / 8); the lower index keeps the sum.
-    // Both lanes form partner + own', own' = own with its sign flipped in the upper lane:
-    // x_i + x_{i+h} (addition commutes) and x_i + (-x_{i+h}), the same binary32 operation
-    // as x_i - x_{i+h}.  One add per element and stage, the exchange folded into it as a
-    // DPP operand.
-    auto cross = [&](auto d_tag) {
-      constexpr int D = decltype(d_tag)::value;
-      if constexpr (D < N / 8) {
-        const unsigned flip = (llane & D) ? 0x80000000u : 0u;
-        // all sign flips of the stage first: a DPP add waits out two cycles after any
-        // write of either of its operands
-        float own[UNROLL][8];
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) own[u][i] = __uint_as_float(__float_as_uint(v[u][i]) ^ flip);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int u = 0; u < UNROLL; ++u)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            float partner;
-            if constexpr (D == 4 && RELABEL)   // logical lane ^ 4 is physical lane ^ 7
-              partner = __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v[u][i]), 0x141, 0xF, 0xF, true));
-            else
-              partner = lane_xor<D>(v[u][i], lane);
-            v[u][i] = __fadd_rn(partner, own[u][i]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    cross(std::integral_constant<int, 1>{});
-    cross(std::integral_constant<int, 2>{});
-    cross(std::integral_constant<int, 4>{});
-    cross(std::integral_constant<int, 8>{});
-    cross(std::integral_constant<int, 16>{});
-#pragma unroll
-    for (int u = 0; u < UNROLL; ++u) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v[u][i] = __fmul_rn(v[u][i], kNorm);
-      // MXFP4 of the rotated binary32 values (as mx_quantize_kernel)
-      unsigned m = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) m = max(m, __float_as_uint(v[u][i]) & 0x7FFFFFFFu);
-      const unsigned amax = quad_max_u32(m);
-      const unsigned e = amax >> 23;
-      const unsigned s = UOS ? scale_byte_uos(e, (amax & 0x7FFFFFu) > 0x680000u ? 1u : 0u) : scale_byte_from_exp(e);
-      const float scale = e8m0_to_f32(s);
-      unsigned r = 0;
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][0], v[u][1], scale, 0);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][2], v[u][3], scale, 1);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][4], v[u][5], scale, 2);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[u][6], v[u][7], scale, 3);
-      if (ok[u]) {
         __builtin_nontemporal_store(r, reinterpret_cast<unsigned*>(codes + co[u]));
         if (q == 0) scales[so[u]] = (uint8_t)s;
       }
@@ -583,39 +393,6 @@ hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t 
     uos ? go(mx_quantize_kernel<true, true>) : go(mx_quantize_kernel<true, false>);
   else
     uos ? go(mx_quantize_kernel<false, true>) : go(mx_quantize_kernel<false, false>);
-  return hipGetLastError();
-}
-
-hipError_t launch_quantize_mxfp4_rotated(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x, int n,
-                                         uint8_t* codes, int64_t ld_codes, uint8_t* scales, int64_t ld_scales,
-                                         bool uos, hipStream_t stream) {
-  const int64_t bpr = cols / 32;
-  const int64_t total = rows * bpr;
-  if (total == 0) return hipSuccess;
-  const int contiguous = (ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr) ? 1 : 0;
-  constexpr int T = kRotThreads, U = kRotUnroll;
-  const int grid = grid_for(total, T / 4 * U);
-  auto go = [&](auto kernel) {
-    hipLaunchKernelGGL(kernel, dim3(grid), dim3(T), 0, stream, x, ld_x, codes, ld_codes, scales, ld_scales,
-                       (uint32_t)bpr, total, contiguous);
-  };
-  auto pick_rule = [&](auto f32_tag, auto n_tag) {
-    constexpr bool F = decltype(f32_tag)::value;
-    constexpr int NN = decltype(n_tag)::value;
-    uos ? go(mx_quantize_rot_kernel<F, NN, true, T, U>) : go(mx_quantize_rot_kernel<F, NN, false, T, U>);
-  };
-  auto pick_n = [&](auto f32_tag) {
-    if (n == 16)
-      pick_rule(f32_tag, std::integral_constant<int, 16>{});
-    else if (n == 64)
-      pick_rule(f32_tag, std::integral_constant<int, 64>{});
-    else
-      pick_rule(f32_tag, std::integral_constant<int, 256>{});
-  };
-  if (f32)
-    pick_n(std::true_type{});
-  else
-    pick_n(std::false_type{});
   return hipGetLastError();
 }
 
