@@ -4,7 +4,7 @@ against the oracle: bit-exact codes and scales.
 * bf16 inputs: heavy-tailed values and values spread over the whole exponent range
   (subnormal binary32 intermediates included), every block size and both scale rules;
 * binary32 inputs over a wide exponent range;
-* row-strided input and ragged row counts;
+* row-strided input and ragged row counts, partial 64-block spans for both input types;
 * rows of the Wan2.2-shaped activations at full size;
 * the W4A4 chain with both operands rotated, on the Wan2.2 FFN-down shape at reduced M:
   SQNR against the unrotated bf16 reference, GPU chain vs oracle chain within 0.01 dB,
@@ -68,6 +68,28 @@ def test_hadamard_strided_and_ragged(gpu, rows, cols, pad, n):
     full = torch.randn(rows, cols + pad, device="cuda", generator=g).mul_(5.0).to(torch.bfloat16)
     x = full[:, :cols]
     _check(gpu, x, bf16_bits_to_f32(to_np_bf16_bits(x)), n, "ocp", "strided")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("pad", [0, 32])
+def test_hadamard_partial_spans(gpu, dtype, n, pad):
+    """45 x 768: 1080 blocks, so the last 64-block span of a wave is partial (56 blocks);
+    packed rows and row-strided rows (spans cross row ends), both input types, both rules."""
+    rng = np.random.default_rng(51 + n + pad)
+    rows, cols = 45, 768
+    m = rng.standard_t(3, (rows, cols + pad)) * np.ldexp(1.0, rng.integers(-20, 20, (rows, 1)))
+    full32 = m.astype(np.float32)
+    if dtype == "bf16":
+        bits = (full32.view(np.uint32) >> 16).astype(np.uint16)
+        full = bf16_from_bits(bits)
+        host = bf16_bits_to_f32(bits[:, :cols])
+    else:
+        full = torch.from_numpy(full32).cuda()
+        host = full32[:, :cols]
+    x = full[:, :cols]
+    for rule in ("ocp", "uos"):
+        _check(gpu, x, np.ascontiguousarray(host), n, rule, f"partial spans {dtype} pad={pad}")
 
 
 def test_hadamard_workload_rows(gpu):
