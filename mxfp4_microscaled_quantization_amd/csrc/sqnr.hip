@@ -6,7 +6,8 @@
 // every element of two bf16 matrices, dB = 10 log10(S / N).
 //
 // Deterministic by construction: the grid size is a function of the element count only,
-// each thread owns a fixed strided set of 8-element chunks and accumulates in binary64
+// each thread owns a fixed set of 8-element chunks (per pass, chunk u * 256 + t of its
+// workgroup's run of 4 x 256 consecutive chunks, u = 0 .. 3 in order) and accumulates in binary64
 // (values widened exactly; differences, squares and sums in binary64, so no intermediate
 // overflows or underflows for any finite bf16 input), workgroups
 // reduce in a fixed tree order into the workspace, and one workgroup sums the workspace
@@ -41,33 +42,60 @@ __device__ __forceinline__ void block_reduce2(double& s, double& n, double* sh) 
   n = sh[kThreads];
 }
 
+// Each workgroup pass covers 4 x 256 consecutive chunks, every load of the pass issued
+// before the arithmetic (84 % of HBM against 78 % with one chunk per thread and pass, and
+// 74 % with four chunks a grid stride apart); packed rows take linear offsets.
+constexpr int kSqUnroll = 4;
+
+template <bool CONTIG>
 __global__ __launch_bounds__(kThreads) void sqnr_partial_kernel(const uint16_t* __restrict__ ref,
                                                                 const uint16_t* __restrict__ test, int64_t ld_ref,
                                                                 int64_t ld_test, uint32_t chunks_per_row,
                                                                 int64_t total_chunks, double* __restrict__ ws) {
+  constexpr int U = kSqUnroll;
   __shared__ double sh[2 * kThreads];
   double s = 0.0, n = 0.0;
-  const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t c = (int64_t)blockIdx.x * kThreads + threadIdx.x; c < total_chunks; c += stride) {
-    const uint32_t cc = (uint32_t)c;
-    const uint32_t row = cc / chunks_per_row;
-    const uint32_t col = (cc - row * chunks_per_row) * 8;
-    const v4i r = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(ref + (int64_t)row * ld_ref + col));
-    const v4i q = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(test + (int64_t)row * ld_test + col));
+  const int64_t step = (int64_t)gridDim.x * kThreads * U;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * U + threadIdx.x; c0 < total_chunks; c0 += step) {
+    v4i r[U], q[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // bf16 -> binary32 -> binary64 is exact (a bf16 is the high half of a binary32);
-      // differences, squares and sums are binary64: every finite bf16 lies in
-      // [2^-133, 2^128), so no square overflows or underflows
-      const double r0 = (double)__uint_as_float((unsigned)r[i] << 16);
-      const double r1 = (double)__uint_as_float((unsigned)r[i] & 0xFFFF0000u);
-      const double q0 = (double)__uint_as_float((unsigned)q[i] << 16);
-      const double q1 = (double)__uint_as_float((unsigned)q[i] & 0xFFFF0000u);
-      const double d0 = r0 - q0, d1 = r1 - q1;
-      s = fma(r0, r0, s);
-      s = fma(r1, r1, s);
-      n = fma(d0, d0, n);
-      n = fma(d1, d1, n);
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + u * kThreads;
+      r[u] = v4i{0, 0, 0, 0};
+      q[u] = v4i{0, 0, 0, 0};
+      if (c < total_chunks) {
+        int64_t o_ref, o_test;
+        if (CONTIG) {
+          o_ref = o_test = c * 8;
+        } else {
+          const uint32_t cc = (uint32_t)c;
+          const uint32_t row = cc / chunks_per_row;
+          const uint32_t col = (cc - row * chunks_per_row) * 8;
+          o_ref = (int64_t)row * ld_ref + col;
+          o_test = (int64_t)row * ld_test + col;
+        }
+        r[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(ref + o_ref));
+        q[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(test + o_test));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // bf16 -> binary32 -> binary64 is exact (a bf16 is the high half of a binary32);
+        // differences, squares and sums are binary64: every finite bf16 lies in
+        // [2^-133, 2^128), so no square overflows or underflows (a chunk past the end
+        // reads zeros and adds nothing)
+        const double r0 = (double)bf16_lo_f32(r[u][i]);
+        const double r1 = (double)bf16_hi_f32(r[u][i]);
+        const double q0 = (double)bf16_lo_f32(q[u][i]);
+        const double q1 = (double)bf16_hi_f32(q[u][i]);
+        const double d0 = r0 - q0, d1 = r1 - q1;
+        s = fma(r0, r0, s);
+        s = fma(r1, r1, s);
+        n = fma(d0, d0, n);
+        n = fma(d1, d1, n);
+      }
     }
   }
   block_reduce2(s, n, sh);
@@ -140,8 +168,9 @@ hipError_t launch_sqnr(const uint16_t* ref, const uint16_t* test, int64_t rows, 
   if (groups > kMaxGroups) groups = kMaxGroups;
   if (groups < 1) groups = 1;
   double* w = static_cast<double*>(ws);
-  hipLaunchKernelGGL(sqnr_partial_kernel, dim3((unsigned)groups), dim3(kThreads), 0, stream, ref, test, ld_ref,
-                     ld_test, (uint32_t)(cpr > 0 ? cpr : 1), total, w);
+  const bool contig = ld_ref == cols && ld_test == cols;
+  hipLaunchKernelGGL(contig ? sqnr_partial_kernel<true> : sqnr_partial_kernel<false>, dim3((unsigned)groups),
+                     dim3(kThreads), 0, stream, ref, test, ld_ref, ld_test, (uint32_t)(cpr > 0 ? cpr : 1), total, w);
   hipLaunchKernelGGL(sqnr_final_kernel, dim3(1), dim3(kThreads), 0, stream, w, (int)groups, out3);
   return hipGetLastError();
 }
