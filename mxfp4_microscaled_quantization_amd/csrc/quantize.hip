@@ -29,12 +29,16 @@ namespace {
 
 constexpr int kThreads = 256;         // absmax_kernel
 // mx_quantize_kernel: 512-thread workgroups, 8 blocks in flight per quad (77 % of HBM
-// against 63 % with 256 threads and 4 blocks); the FP8 kernel runs 1024-thread workgroups.
+// against 63 % with 256 threads and 4 blocks).
 constexpr int kMxThreads = 512;
 constexpr int kMxUnroll = 8;
 constexpr int kMxBlocksPerIter = kMxThreads / 4 * kMxUnroll;
-constexpr int kFp8Threads = 1024;
-constexpr int kFp8Unroll = 2;     // chunks of 16 per lane per pass (72 % of HBM against 69 % for one)
+// fp8_quantize_kernel: units of 8 elements (one 16-byte bf16 load and one 8-byte store per
+// lane, both contiguous across the wave), 4 units per lane per pass in 512-thread
+// workgroups: 75-78 % of HBM against 72-74 % for 16-element units (two 16-byte loads per
+// lane, each instruction covering half of every line it touches)
+constexpr int kFp8Threads = 512;
+constexpr int kFp8Unroll = 4;
 // dequantize_kernel: 4 quarter-blocks per lane per pass in 1024-thread workgroups, loads
 // first (72 % of HBM; 512 threads with 2, 8 or 16 quarters and 256 threads with 8 within
 // 4 % of it; 58 % for one quarter per lane and 256 threads)
@@ -138,75 +142,70 @@ __global__ __launch_bounds__(kMxThreads) void mx_quantize_kernel(
 // ---------------------------------------------------------------------------------
 // Static FP8 E4M3: q = E4M3_RNE(clamp(fl32(x * inv_scale), -448, 448)).  The clamp makes
 // the gfx950 conversion saturate (it returns NaN past the rounding edge otherwise); the
-// clamp keeps the sign of zero.  16 elements per lane, one 16-byte store.
+// clamp keeps the sign of zero.  8 elements per lane and unit: one 16-byte bf16 load, one
+// 8-byte store.
 template <bool F32>
 __global__ __launch_bounds__(kFp8Threads) void fp8_quantize_kernel(
     const void* __restrict__ x, int64_t ld_x, float inv_scale, uint8_t* __restrict__ out, int64_t ld_q,
-    uint32_t chunks_per_row, int64_t total_chunks, int contiguous) {
-  // each lane takes kFp8Unroll chunks of 16 elements per pass, loads first
-  const int64_t stride = (int64_t)gridDim.x * kFp8Threads * kFp8Unroll;
-  for (int64_t c0 = (int64_t)blockIdx.x * kFp8Threads * kFp8Unroll + threadIdx.x; c0 < total_chunks; c0 += stride) {
-    v4i d[kFp8Unroll][4];
-    int64_t qo[kFp8Unroll];
-    bool ok[kFp8Unroll];
+    uint32_t units_per_row, int64_t total_units, int contiguous) {
+  constexpr int T = kFp8Threads, U = kFp8Unroll;
+  const int64_t stride = (int64_t)gridDim.x * T * U;
+  for (int64_t c0 = (int64_t)blockIdx.x * T * U + threadIdx.x; c0 < total_units; c0 += stride) {
+    v4i d[U][2];
+    int64_t qo[U];
+    bool ok[U];
 #pragma unroll
-    for (int u = 0; u < kFp8Unroll; ++u) {
-      const int64_t c = c0 + (int64_t)u * kFp8Threads;
-      ok[u] = c < total_chunks;
+    for (int u = 0; u < U; ++u) {
+      const int64_t c = c0 + (int64_t)u * T;
+      ok[u] = c < total_units;
       int64_t xo;
       if (contiguous) {
-        xo = c * 16;
-        qo[u] = c * 16;
+        xo = c * 8;
+        qo[u] = c * 8;
       } else {
         const uint32_t cc = (uint32_t)c;
-        const uint32_t row = cc / chunks_per_row;
-        const uint32_t col = cc - row * chunks_per_row;
-        xo = (int64_t)row * ld_x + col * 16;
-        qo[u] = (int64_t)row * ld_q + col * 16;
+        const uint32_t row = cc / units_per_row;
+        const uint32_t col = cc - row * units_per_row;
+        xo = (int64_t)row * ld_x + col * 8;
+        qo[u] = (int64_t)row * ld_q + col * 8;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) d[u][i] = v4i{0, 0, 0, 0};
+      d[u][0] = v4i{0, 0, 0, 0};
+      d[u][1] = v4i{0, 0, 0, 0};
       if (ok[u]) {
         if (F32) {
           const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) d[u][i] = __builtin_nontemporal_load(p + i);
-        } else {
-          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo);
           d[u][0] = __builtin_nontemporal_load(p);
           d[u][1] = __builtin_nontemporal_load(p + 1);
+        } else {
+          d[u][0] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo));
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kFp8Unroll; ++u) {
-      float v[16];
+    for (int u = 0; u < U; ++u) {
+      float v[8];
       if (F32) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) v[4 * i + jj] = __int_as_float(d[u][i][jj]);
+        for (int jj = 0; jj < 4; ++jj) { v[jj] = __int_as_float(d[u][0][jj]); v[4 + jj] = __int_as_float(d[u][1][jj]); }
       } else {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int jj = 0; jj < 4; ++jj) {
-            v[8 * i + 2 * jj] = __uint_as_float((unsigned)d[u][i][jj] << 16);
-            v[8 * i + 2 * jj + 1] = __uint_as_float((unsigned)d[u][i][jj] & 0xFFFF0000u);
-          }
+        for (int jj = 0; jj < 4; ++jj) {
+          v[2 * jj] = bf16_lo_f32(d[u][0][jj]);
+          v[2 * jj + 1] = bf16_hi_f32(d[u][0][jj]);
+        }
       }
-      v4i o;
+      v2u o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < 2; ++i) {
         float y[4];
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) y[jj] = __builtin_amdgcn_fmed3f(v[4 * i + jj] * inv_scale, -448.0f, 448.0f);
         int r = 0;
         r = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], r, false);
         r = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], r, true);
-        o[i] = r;
+        o[i] = (unsigned)r;
       }
-      if (ok[u]) __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(out + qo[u]));
+      if (ok[u]) __builtin_nontemporal_store(o, reinterpret_cast<v2u*>(out + qo[u]));
     }
   }
 }
@@ -398,17 +397,17 @@ hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t 
 
 hipError_t launch_quantize_fp8(const void* x, bool f32, int64_t rows, int64_t cols, int64_t ld_x,
                                float inv_scale, uint8_t* q, int64_t ld_q, hipStream_t stream) {
-  const int64_t cpr = cols / 16;
-  const int64_t total = rows * cpr;
+  const int64_t upr = cols / 8;
+  const int64_t total = rows * upr;
   if (total == 0) return hipSuccess;
   const int contiguous = (ld_x == cols && ld_q == cols) ? 1 : 0;
   const int grid = grid_for(total, kFp8Threads * kFp8Unroll);
   if (f32)
     hipLaunchKernelGGL(fp8_quantize_kernel<true>, dim3(grid), dim3(kFp8Threads), 0, stream, x, ld_x, inv_scale,
-                       q, ld_q, (uint32_t)cpr, total, contiguous);
+                       q, ld_q, (uint32_t)upr, total, contiguous);
   else
     hipLaunchKernelGGL(fp8_quantize_kernel<false>, dim3(grid), dim3(kFp8Threads), 0, stream, x, ld_x, inv_scale,
-                       q, ld_q, (uint32_t)cpr, total, contiguous);
+                       q, ld_q, (uint32_t)upr, total, contiguous);
   return hipGetLastError();
 }
 
