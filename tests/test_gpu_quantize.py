@@ -4,7 +4,8 @@
   it can meet), random binary32 patterns under random scales, the tiny workload (fp32),
   the FLUX-shaped activations and weights in full, rows sampled from the Wan2.2-shaped
   activations at full size, ragged / strided layouts, and determinism.
-* FP8 E4M3 (static): every bf16 pattern under several multipliers, workload shapes.
+* FP8 E4M3 (static): every bf16 pattern under several multipliers, workload shapes, binary32
+  and strided inputs and outputs with a partial last pass.
 * Dequantization: every code byte under every scale byte.
 """
 
@@ -177,6 +178,33 @@ def test_fp8_static_scale_workload_rows(gpu):
     torch.cuda.synchronize()
     np.testing.assert_array_equal(to_np_u8(q), oracle.quantize_fp8(host, inv_s))
     assert (to_np_u8(q) & 0x7F).max() == 0x7E          # the tensor maximum maps onto 448
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("pad_in,pad_out", [(0, 0), (48, 32)])
+def test_fp8_input_types_strided_and_ragged(gpu, dtype, pad_in, pad_out):
+    """Binary32 and bf16 input, packed or row-strided input and output, 37 x 784: 3626
+    8-element units, so the kernel's last pass is partial and strided units cross rows."""
+    rng = np.random.default_rng(61 + pad_in)
+    rows, cols = 37, 784
+    m = rng.standard_t(3, (rows, cols + pad_in)) * np.ldexp(1.0, rng.integers(-12, 12, (rows, 1)))
+    full32 = m.astype(np.float32)
+    if dtype == "bf16":
+        bits = (full32.view(np.uint32) >> 16).astype(np.uint16)
+        full = bf16_from_bits(bits)
+        host = bf16_bits_to_f32(bits[:, :cols])
+    else:
+        full = torch.from_numpy(full32).cuda()
+        host = full32[:, :cols]
+    x = full[:, :cols]
+    inv_s = float(oracle.fp8_static_scales(np.max(np.abs(host)))[1])
+    qfull = torch.full((rows, cols + pad_out), 0xA5, dtype=torch.uint8, device="cuda")
+    announce(f"mxq_quantize_fp8 {dtype} pad_in={pad_in} pad_out={pad_out} {rows}x{cols}")
+    q = gpu.quantize_fp8(x, inv_s, out=qfull[:, :cols])
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np_u8(q), oracle.quantize_fp8(np.ascontiguousarray(host), np.float32(inv_s)))
+    if pad_out:
+        assert (to_np_u8(qfull[:, cols:]) == 0xA5).all()      # nothing past the viewed columns
 
 
 def test_absmax_fp32_and_strided(gpu):
