@@ -21,6 +21,8 @@
 // gfx950 conversion v_cvt_scalef32_pk_fp4_f32, which computes round-to-nearest-even of
 // x / scale with saturation for power-of-two scales (including the subnormal 2^-127), two
 // elements per instruction (bf16 inputs are widened exactly first).
+#include <type_traits>
+
 #include "mxq_device.hpp"
 #include "mxq_internal.hpp"
 
@@ -28,10 +30,11 @@ namespace mxq {
 namespace {
 
 constexpr int kThreads = 256;         // absmax_kernel
-// mx_quantize_kernel: 512-thread workgroups, 8 blocks in flight per quad (77 % of HBM
-// against 63 % with 256 threads and 4 blocks).
-constexpr int kMxThreads = 512;
-constexpr int kMxUnroll = 8;
+// mx_quantize_kernel: 1024-thread workgroups, 4 blocks in flight per quad, buffer loads
+// for packed rows (80 % of HBM; 512 threads with 8 blocks 77 %, 256 threads with 8 or 16
+// blocks 72-74 %)
+constexpr int kMxThreads = 1024;
+constexpr int kMxUnroll = 4;
 constexpr int kMxBlocksPerIter = kMxThreads / 4 * kMxUnroll;
 // fp8_quantize_kernel: units of 8 elements (one 16-byte bf16 load and one 8-byte store per
 // lane, both contiguous across the wave), 4 units per lane per pass in 512-thread
@@ -50,50 +53,62 @@ constexpr int kDq8Threads = 1024;
 constexpr int kDq8Unroll = 4;
 
 // ---------------------------------------------------------------------------------
-// MXFP4 quantization.  F32 selects binary32 input (else bf16); UOS the 7.25 boundary.
-template <bool F32, bool UOS>
+// MXFP4 quantization.  F32 selects binary32 input (else bf16); UOS the 7.25 boundary;
+// CONTIG packed rows (linear offsets, buffer loads), else one 32-bit division per block.
+template <bool F32, bool UOS, bool CONTIG>
 __global__ __launch_bounds__(kMxThreads) void mx_quantize_kernel(
     const void* __restrict__ x, int64_t ld_x, uint8_t* __restrict__ codes, int64_t ld_codes,
-    uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks,
-    int contiguous) {
+    uint8_t* __restrict__ scales, int64_t ld_scales, uint32_t blocks_per_row, int64_t total_blocks) {
+  constexpr int T = kMxThreads, U = kMxUnroll, BPI = kMxBlocksPerIter;
   const int tid = threadIdx.x;
-  const int q = tid & 3;                       // quarter of the block owned by this lane
-  const int64_t stride = (int64_t)gridDim.x * kMxBlocksPerIter;
-  for (int64_t base = (int64_t)blockIdx.x * kMxBlocksPerIter; base < total_blocks; base += stride) {
-    int64_t xo[kMxUnroll], co[kMxUnroll], so[kMxUnroll];
-    bool ok[kMxUnroll];
-    v4i d0[kMxUnroll], d1[kMxUnroll];
+  const int q = tid & 3;
+  const int64_t stride = (int64_t)gridDim.x * BPI;
+  for (int64_t base = (int64_t)blockIdx.x * BPI; base < total_blocks; base += stride) {
+    v4i d0[U], d1[U];
+    int64_t co[U], so[U];
+    bool ok[U];
+    // packed rows: the pass's BPI blocks are one span, read through a buffer descriptor
+    // whose range check zero-fills past the last block (no per-load branch)
+    const int64_t left = total_blocks - base;
+    const uint32_t nb = left <= 0 ? 0u : (uint32_t)(left < BPI ? left : BPI);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(x) + base * (F32 ? 128 : 64), nb * (F32 ? 128u : 64u));
 #pragma unroll
-    for (int u = 0; u < kMxUnroll; ++u) {
-      const int64_t b = base + u * (kMxThreads / 4) + (tid >> 2);
+    for (int u = 0; u < U; ++u) {
+      const int lb = u * (T / 4) + (tid >> 2);          // block within the pass
+      const int64_t b = base + lb;
       ok[u] = b < total_blocks;
-      if (contiguous) {
-        xo[u] = b * 32 + q * 8;
+      if (CONTIG) {
         co[u] = b * 16 + q * 4;
         so[u] = b;
+        if (F32) {
+          d0[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lb * 128 + q * 32, 0, 2));
+          d1[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lb * 128 + q * 32 + 16, 0, 2));
+        } else {
+          d0[u] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, lb * 64 + q * 16, 0, 2));
+          d1[u] = v4i{0, 0, 0, 0};
+        }
       } else {
         const uint32_t bb = (uint32_t)b;
         const uint32_t row = bb / blocks_per_row;
         const uint32_t blk = bb - row * blocks_per_row;
-        xo[u] = (int64_t)row * ld_x + blk * 32 + q * 8;
+        const int64_t xo = (int64_t)row * ld_x + blk * 32 + q * 8;
         co[u] = (int64_t)row * ld_codes + blk * 16 + q * 4;
         so[u] = (int64_t)row * ld_scales + blk;
-      }
-      d0[u] = v4i{0, 0, 0, 0};
-      d1[u] = v4i{0, 0, 0, 0};
-      if (ok[u]) {
-        if (F32) {
-          const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo[u]);
-          d0[u] = __builtin_nontemporal_load(p);
-          d1[u] = __builtin_nontemporal_load(p + 1);
-        } else {
-          d0[u] = __builtin_nontemporal_load(
-              reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo[u]));
+        d0[u] = v4i{0, 0, 0, 0};
+        d1[u] = v4i{0, 0, 0, 0};
+        if (ok[u]) {
+          if (F32) {
+            const v4i* p = reinterpret_cast<const v4i*>(static_cast<const float*>(x) + xo);
+            d0[u] = __builtin_nontemporal_load(p);
+            d1[u] = __builtin_nontemporal_load(p + 1);
+          } else {
+            d0[u] = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(static_cast<const uint16_t*>(x) + xo));
+          }
         }
       }
     }
 #pragma unroll
-    for (int u = 0; u < kMxUnroll; ++u) {
+    for (int u = 0; u < U; ++u) {
       unsigned amax, e, bump;
       if (F32) {
         unsigned m = 0;
@@ -123,15 +138,12 @@ __global__ __launch_bounds__(kMxThreads) void mx_quantize_kernel(
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d1[u][0]), __int_as_float(d1[u][1]), scale, 2);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, __int_as_float(d1[u][2]), __int_as_float(d1[u][3]), scale, 3);
       } else {
-        // bf16 pairs are widened exactly to binary32 (a shift / a mask) and converted
-        // with the f32 form, whose destination-byte select places byte k of the word
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][0]), bf16_hi_f32(d0[u][0]), scale, 0);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][1]), bf16_hi_f32(d0[u][1]), scale, 1);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][2]), bf16_hi_f32(d0[u][2]), scale, 2);
         r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, bf16_lo_f32(d0[u][3]), bf16_hi_f32(d0[u][3]), scale, 3);
       }
       if (ok[u]) {
-        // codes are not read again by this kernel: stream them past the caches
         __builtin_nontemporal_store(r, reinterpret_cast<unsigned*>(codes + co[u]));
         if (q == 0) scales[so[u]] = (uint8_t)s;
       }
@@ -382,16 +394,20 @@ hipError_t launch_quantize_mxfp4(const void* x, bool f32, int64_t rows, int64_t 
   const int64_t bpr = cols / 32;
   const int64_t total = rows * bpr;
   if (total == 0) return hipSuccess;
-  const int contiguous = (ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr) ? 1 : 0;
+  const bool contiguous = ld_x == cols && ld_codes == cols / 2 && ld_scales == bpr;
   const int grid = grid_for(total, kMxBlocksPerIter);
   auto go = [&](auto kernel) {
     hipLaunchKernelGGL(kernel, dim3(grid), dim3(kMxThreads), 0, stream, x, ld_x, codes, ld_codes, scales, ld_scales,
-                       (uint32_t)bpr, total, contiguous);
+                       (uint32_t)bpr, total);
+  };
+  auto pick = [&](auto f_tag, auto u_tag) {
+    constexpr bool F = decltype(f_tag)::value, R = decltype(u_tag)::value;
+    contiguous ? go(mx_quantize_kernel<F, R, true>) : go(mx_quantize_kernel<F, R, false>);
   };
   if (f32)
-    uos ? go(mx_quantize_kernel<true, true>) : go(mx_quantize_kernel<true, false>);
+    uos ? pick(std::true_type{}, std::true_type{}) : pick(std::true_type{}, std::false_type{});
   else
-    uos ? go(mx_quantize_kernel<false, true>) : go(mx_quantize_kernel<false, false>);
+    uos ? pick(std::false_type{}, std::true_type{}) : pick(std::false_type{}, std::false_type{});
   return hipGetLastError();
 }
 
