@@ -267,9 +267,10 @@ __global__ __launch_bounds__(kThreads) void absmax_kernel(const void* __restrict
 }
 
 // ---------------------------------------------------------------------------------
-// MXFP4 -> bf16: e2m1(code) * 2^(s - 127).  The product is formed in binary32 (exact:
-// at most 3 significant bits, exponent within binary32's range down to the subnormal
-// 2^-128) and narrowed to bf16 with round to nearest even (exact in range).
+// MXFP4 -> bf16: bf16_RNE(e2m1(code) * 2^(s - 127)).  The product has at most 2
+// significant bits and lies in bf16's exponent range down to the subnormal 2^-128, so it
+// is exact unless it overflows (to +-inf); scale byte 0xFF gives NaN.  One gfx950
+// conversion per code byte does the scaling and the rounding.
 // CONTIG: codes, scales and output are packed rows (offsets are linear in the quarter
 // index); otherwise the row comes from one 32-bit division (quarters < 2^32).
 template <bool CONTIG>
@@ -307,22 +308,18 @@ __global__ __launch_bounds__(kDqThreads) void dequantize_kernel(
     }
 #pragma unroll
     for (int u = 0; u < kDqUnroll; ++u) {
-      // 2 * |e2m1| for magnitude codes 0..7 is 0,1,2,3,4,6,8,12: one nibble each
+      // v_cvt_scalef32_pk_bf16_fp4: the two E2M1 nibbles of byte i (low nibble first) times
+      // the binary32 scale, rounded once to bf16.  Checked on the GPU against the exact
+      // product for every code byte under every scale byte: exact RNE, the subnormal
+      // 2^-127 scale taken as such, overflow to +-inf, -0 kept; a NaN scale (byte 0xFF)
+      // gives NaN.
       const unsigned sv = s[u];
-      const float half_scale = sv >= 2 ? __uint_as_float((sv - 1) << 23) : (sv == 1 ? 0x1p-127f : 0x1p-128f);
-      const float sc = sv == 255 ? __uint_as_float(0x7FC00000u) : half_scale;
+      const float sc = sv == 255 ? __uint_as_float(0x7FC00000u) : e8m0_to_f32(sv);
       v4i o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float f[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const unsigned code = (c[u] >> (8 * i + 4 * h)) & 0xF;
-          const float mag = (float)((0xC8643210u >> (4 * (code & 7))) & 0xF) * sc;
-          f[h] = (code & 8) ? -mag : mag;
-        }
-        o[i] = (int)pack_bf16x2(f[0], f[1]);
-      }
+      o[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], sc, 0));
+      o[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], sc, 1));
+      o[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], sc, 2));
+      o[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c[u], sc, 3));
       // the output is not read again here: stream it past the caches
       if (ok[u]) __builtin_nontemporal_store(o, reinterpret_cast<v4i*>(y + yo[u]));
     }
