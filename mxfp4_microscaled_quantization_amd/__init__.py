@@ -21,10 +21,13 @@ __all__ = [
     "lib", "MxqError", "quantize", "quantize_into", "quantize_hadamard", "SCALE_RULES", "quantize_fp8", "absmax", "fp8_static_scales",
     "gemm_w4a4", "gemm_w4a4_fused", "gemm_w4a8", "gemm_bf16", "sqnr", "sqnr_noalloc", "sqnr_workspace_bytes", "dequantize", "dequantize_fp8",
     "mfma_ceiling", "MFMA_FLOP", "check_buffer",
-    "LIB_PATH", "ABI_SYMBOLS",
+    "LIB_PATH", "ABI_SYMBOLS", "ABI_VERSION",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmxq.so")
+
+#: MXQ_ABI_VERSION of include/mxq.h that the signatures below describe
+ABI_VERSION = 2
 
 MXQ_OK, MXQ_ERR_INVALID_ARG, MXQ_ERR_UNSUPPORTED, MXQ_ERR_HIP = 0, 1, 2, 3
 MXQ_F32, MXQ_BF16 = 0, 1
@@ -69,6 +72,10 @@ def _load():
         fn = getattr(handle, name)
         fn.restype = res
         fn.argtypes = args
+    found = handle.mxq_abi_version()
+    if found != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} reports ABI version {found}, this binding expects {ABI_VERSION}: "
+                          "rebuild it with `python mxfp4_microscaled_quantization_amd/build.py`")
     return handle
 
 

@@ -41,7 +41,10 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version():
-    assert mxq.lib.mxq_abi_version() == 2
+    """The header's MXQ_ABI_VERSION, the library's and the binding's agree."""
+    header = open(os.path.join(ROOT, "include", "mxq.h")).read()
+    declared = int(re.search(r"#define MXQ_ABI_VERSION (\d+)", header).group(1))
+    assert mxq.lib.mxq_abi_version() == declared == mxq.ABI_VERSION == 2
 
 
 def _err():
