@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kRotThreads) void mx_quantize_rot_kernel(
         // the wave's 64 blocks are one span; loads past the last block read zero
         const int64_t left = total_blocks - wb;
         const uint32_t nb = left <= 0 ? 0u : (uint32_t)(left < 64 ? left : 64) * (RU * 16);
-        const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(x) + wb * (RU * 16), nb);
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(static_cast<const char*>(x) + (nb ? wb * (RU * 16) : 0), nb);
 #pragma unroll
         for (int j = 0; j < RU; ++j)   // aux 2: non-temporal, the input is read once
           raw[u][j] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(rs, j * 1024 + lane * 16, 0, 2));
@@ -185,8 +185,9 @@ __global__ __launch_bounds__(kRotThreads) void mx_quantize_rot_kernel(
         // stores past the last block are dropped by the buffer range check
         const int64_t left = total_blocks - wb;
         const uint32_t nb = left <= 0 ? 0u : (uint32_t)(left < 64 ? left : 64);
-        const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + wb * 16, nb * 16);
-        const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scales + wb, nb);
+        // (a wave past the last block gets an empty range at the buffer's start)
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(codes + (nb ? wb * 16 : 0), nb * 16);
+        const __amdgpu_buffer_rsrc_t rsc = make_rsrc(scales + (nb ? wb : 0), nb);
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(v4u, r), rc, slot * 16, 0, 2);
         __builtin_amdgcn_raw_buffer_store_b8((unsigned char)s, rsc, slot, 0, 2);
       } else {
