@@ -220,17 +220,22 @@ def test_absmax_fp32_and_strided(gpu):
 # ---------------------------------------------------------------------------- dequantize
 
 def test_dequantize_every_code_and_scale(gpu):
-    codes = np.tile(np.arange(256, dtype=np.uint8), (255, 1))          # [255, 256] -> K = 512
-    scales = np.tile(np.arange(255, dtype=np.uint8)[:, None], (1, 16))  # one scale byte per row
+    """Every code byte under every scale byte (one scale per row), bit for bit: products
+    past the largest bf16 round to +-inf, and scale byte 0xFF (the E8M0 NaN) gives NaN."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))          # [256, 256] -> K = 512
+    scales = np.tile(np.arange(256, dtype=np.uint8)[:, None], (1, 16))  # one scale byte per row
     cg, sg = torch.from_numpy(codes).cuda(), torch.from_numpy(scales).cuda()
     announce("mxq_dequantize exhaustive")
     y = gpu.dequantize(cg, sg, 512)
     torch.cuda.synchronize()
     ref = oracle.dequantize_mxfp4(codes, scales, 512)
-    finite = np.isfinite(ref) & (np.abs(ref) < 3.3e38)
-    ref_bits = oracle.f64_to_bf16_bits(np.where(finite, ref, 0.0))
+    nan = np.isnan(ref)
+    assert nan.sum() == 512 and nan[255].all()                           # exactly the 0xFF row
+    ref_bits = oracle.f64_to_bf16_bits(np.where(nan, 0.0, ref))
     got = to_np_bf16_bits(y)
-    np.testing.assert_array_equal(got[finite], ref_bits[finite])
+    np.testing.assert_array_equal(got[~nan], ref_bits[~nan])
+    assert (np.abs(ref[~nan]) >= 2.0 ** 128).any()                        # the overflow cases are in
+    assert np.all((got[nan] & 0x7F80) == 0x7F80) and np.all((got[nan] & 0x7F) != 0)
 
 
 def test_dequantize_workload_rows_and_strided_output(gpu):
