@@ -83,7 +83,9 @@ typedef enum { MXQ_F32 = 0, MXQ_BF16 = 1, MXQ_DTYPE_MAX_ENUM = 0x7FFFFFFF } mxq_
  *   field, i.e. X = 2^(clamp(floor(log2 amax) - 2, -127, 127)), all-zero block -> 0x00;
  *   code = E2M1 round-to-nearest-even of x / X, saturated to +-6, sign bit from x.
  * x      : `rows` rows of `cols` elements of type `dt`, row pitch `ld_x` elements.
- *          Base and row pitch in bytes must be multiples of 16.  Finite values only.
+ *          Base and row pitch in bytes must be multiples of 16.  Finite values only: a
+ *          block holding an infinity or a NaN gets scale byte 0xFF (the E8M0 NaN) and
+ *          unspecified codes; the other blocks are unaffected.
  * codes  : out, rows x cols/2 bytes, pitch ld_codes bytes (multiple of 16, base 16-aligned).
  * scales : out, rows x cols/32 bytes, pitch ld_scales bytes (any alignment).
  * Errors : cols % 32 != 0, negative sizes, pitches below the row width, NULL pointers,
@@ -123,7 +125,8 @@ mxq_status mxq_quantize_rule(const void* x, mxq_dtype dt, int64_t rows, int64_t 
  * then quantized like binary32 input of mxq_quantize_rule.  Rotating activations here
  * and weights with the same call leaves A W^T unchanged up to that rounding.
  * Arguments, layout and errors as mxq_quantize_rule; cols must be a multiple of block_n
- * (MXQ_ERR_INVALID_ARG); another block_n -> MXQ_ERR_UNSUPPORTED.
+ * (MXQ_ERR_INVALID_ARG); another block_n -> MXQ_ERR_UNSUPPORTED.  An infinity or NaN
+ * reaches every element of its run, so every block of that run gets scale byte 0xFF.
  */
 mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                                  int block_n, mxq_scale_rule rule, uint8_t* codes, int64_t ld_codes,

@@ -92,6 +92,33 @@ def test_hadamard_partial_spans(gpu, dtype, n, pad):
         _check(gpu, x, np.ascontiguousarray(host), n, rule, f"partial spans {dtype} pad={pad}")
 
 
+@pytest.mark.parametrize("n", SIZES)
+def test_hadamard_nonfinite_runs_get_the_nan_scale(gpu, n):
+    """Outside the contract, but defined: an infinity or NaN reaches every element of its
+    run of n, so every block of that run gets scale byte 0xFF; other runs are unaffected."""
+    rng = np.random.default_rng(81 + n)
+    x = rng.standard_t(3, (4, 512)).astype(np.float32)
+    x[0, 5] = np.nan
+    x[1, 300] = np.inf
+    x[3, 511] = -np.inf
+    bits = (x.view(np.uint32) >> 16).astype(np.uint16)
+    host = bf16_bits_to_f32(bits)
+    announce(f"mxq_quantize_hadamard non-finite n={n}")
+    codes, scales = gpu.quantize_hadamard(bf16_from_bits(bits), n)
+    torch.cuda.synchronize()
+    gs, gc = to_np_u8(scales), to_np_u8(codes)
+    bad = np.zeros_like(gs, dtype=bool)
+    clean = host.copy()
+    for r, c in ((0, 5), (1, 300), (3, 511)):
+        run = (c // n) * n
+        bad[r, run // 32: (run + n + 31) // 32] = True
+        clean[r, run: run + n] = 0.0
+    assert (gs[bad] == 0xFF).all()
+    rc, rs = oracle.quantize_mxfp4_rotated(clean, n)
+    np.testing.assert_array_equal(gs[~bad], rs[~bad])
+    np.testing.assert_array_equal(gc.reshape(4, 16, 16)[~bad], rc.reshape(4, 16, 16)[~bad])
+
+
 def test_hadamard_workload_rows(gpu):
     name = "wan_ffn_down_sqnr"
     wl = workloads.WORKLOADS[name]

@@ -147,6 +147,40 @@ def test_mxfp4_deterministic(gpu):
     assert torch.equal(c1, c2) and torch.equal(s1, s2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_nonfinite_blocks_get_the_nan_scale(gpu, dtype, rule):
+    """Outside the contract (finite input), but defined: a block holding +-inf or NaN gets
+    scale byte 0xFF; every other block is quantized as if the bad blocks were absent."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_t(3, (8, 256)).astype(np.float32)
+    bad = {(0, 0): [(0, 5, np.inf)], (1, 1): [(1, 40, -np.inf)], (2, 3): [(2, 100, np.nan)],
+           (3, 6): [(3, 200, np.inf), (3, 201, np.nan)], (5, 7): [(5, 255, -np.inf), (5, 224, np.inf)]}
+    for hits in bad.values():
+        for r, c, v in hits:
+            x[r, c] = v
+    if dtype == "bf16":
+        bits = (x.view(np.uint32) >> 16).astype(np.uint16)     # truncation keeps inf / NaN
+        xt, host = bf16_from_bits(bits), bf16_bits_to_f32(bits)
+    else:
+        xt, host = torch.from_numpy(x).cuda(), x.copy()
+    announce(f"mxq_quantize non-finite blocks {dtype} {rule}")
+    codes, scales = gpu.quantize(xt, rule)
+    torch.cuda.synchronize()
+    gs, gc = to_np_u8(scales), to_np_u8(codes)
+    clean = host.copy()
+    for (r, b) in bad:
+        assert gs[r, b] == 0xFF, (r, b, hex(gs[r, b]))
+        clean[r, 32 * b: 32 * b + 32] = 0.0
+    rc, rs = oracle.quantize_mxfp4(clean, rule)
+    good = np.ones_like(gs, dtype=bool)
+    for (r, b) in bad:
+        good[r, b] = False
+    np.testing.assert_array_equal(gs[good], rs[good])
+    gcb, rcb = gc.reshape(8, 8, 16), rc.reshape(8, 8, 16)
+    np.testing.assert_array_equal(gcb[good], rcb[good])
+
+
 # ---------------------------------------------------------------------------------- FP8
 
 @pytest.mark.parametrize("inv_s", [1.0, 448.0 / 3.7, 1e-3, 2.0 ** 20, 0.75])
