@@ -142,7 +142,8 @@ mxq_status mxq_quantize_hadamard(const void* x, mxq_dtype dt, int64_t rows, int6
  * x : rows x cols of `dt`, pitch ld_x elements; base and pitch 16-byte aligned.
  * q : out, rows x cols bytes, pitch ld_q bytes; base and pitch multiples of 16.
  * cols must be a multiple of 16.  Errors as for mxq_quantize; inv_scale must be finite
- * and > 0.
+ * and > 0.  Finite values only: an infinity saturates to +-448 like any large value; the
+ * code of a NaN is unspecified.
  */
 mxq_status mxq_quantize_fp8(const void* x, mxq_dtype dt, int64_t rows, int64_t cols, int64_t ld_x,
                             float inv_scale, uint8_t* q, int64_t ld_q, void* stream);

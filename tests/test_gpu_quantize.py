@@ -241,6 +241,18 @@ def test_fp8_input_types_strided_and_ragged(gpu, dtype, pad_in, pad_out):
         assert (to_np_u8(qfull[:, cols:]) == 0xA5).all()      # nothing past the viewed columns
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_fp8_infinities_saturate(gpu, dtype):
+    x = np.array([[np.inf, -np.inf, 1.0, -2.0] * 4], dtype=np.float32)
+    xt = bf16_from_bits((x.view(np.uint32) >> 16).astype(np.uint16)) if dtype == "bf16" else torch.from_numpy(x).cuda()
+    q = to_np_u8(gpu.quantize_fp8(xt, 3.0))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q[0, 0::4], 0x7E)        # +448
+    np.testing.assert_array_equal(q[0, 1::4], 0xFE)        # -448
+    np.testing.assert_array_equal(q[0, 2::4], oracle.quantize_fp8(np.float32([[3.0]]), np.float32(1.0))[0, 0])
+    np.testing.assert_array_equal(q[0, 3::4], oracle.quantize_fp8(np.float32([[-6.0]]), np.float32(1.0))[0, 0])
+
+
 def test_absmax_fp32_and_strided(gpu):
     g = torch.Generator(device="cuda").manual_seed(9)
     full = torch.randn(300, 136, device="cuda", generator=g)
