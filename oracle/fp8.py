@@ -62,7 +62,8 @@ def quantize_fp8(x, inv_s) -> np.ndarray:
     x32 = np.asarray(x, dtype=np.float32)
     if not np.all(np.isfinite(x32)):
         raise ValueError("quantize_fp8: non-finite input is outside the contract")
-    y = x32 * np.float32(inv_s)                 # one binary32 multiply, RNE
+    with np.errstate(over="ignore"):            # a product past binary32 becomes +-inf and saturates
+        y = x32 * np.float32(inv_s)             # one binary32 multiply, RNE
     return e4m3_encode(y.astype(np.float64))
 
 
