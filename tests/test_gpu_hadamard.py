@@ -62,6 +62,24 @@ def test_hadamard_fp32_wide_range(gpu, n):
     _check(gpu, torch.from_numpy(x).cuda(), x, n, "ocp", "fp32 wide")
 
 
+@pytest.mark.parametrize("n", SIZES)
+@pytest.mark.parametrize("rule", ["ocp", "uos"])
+def test_hadamard_tiny_block_boundary(gpu, n, rule):
+    """Blocks whose rotated, normalised maximum lies around 2^-121, with full 24-bit
+    significands reaching down into the subnormal range: the binary32 product by
+    1/sqrt(n) then rounds on the subnormal grid, next to FP4 rounding boundaries of the
+    smallest scales (2^-127 .. 2^-119), and some blocks are all zero."""
+    rng = np.random.default_rng(53 + n)
+    rows, cols = 96, 2048
+    L = {16: 2, 64: 3, 256: 4}[n]
+    m = rng.uniform(1, 2, (rows, cols)) * rng.choice([-1, 1], (rows, cols))
+    top = -121 + L + rng.integers(-8, 9, (rows, 1))   # maximum exponent of each row
+    x = np.ldexp(m, top - rng.integers(0, 30, (rows, cols))).astype(np.float32)
+    x[::7, ::5] = 0.0                                  # some zeros, a few all-zero blocks
+    x[5, :256] = 0.0
+    _check(gpu, torch.from_numpy(x).cuda(), x, n, rule, "fp32 near 2^-121")
+
+
 @pytest.mark.parametrize("rows,cols,pad,n", [(1, 256, 0, 256), (37, 512, 64, 64), (129, 768, 16, 16)])
 def test_hadamard_strided_and_ragged(gpu, rows, cols, pad, n):
     g = torch.Generator(device="cuda").manual_seed(rows + cols)
