@@ -1724,7 +1724,7 @@ hipError_t launch_gemm(GemmMode mode, const void* a, const uint8_t* a_scales, co
   p.vec16 = (ld_out % 8 == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) ? 1 : 0;
   // Short K loops write more output per tile of input: marking those output stores
   // non-temporal keeps the operand panels that neighbouring tiles re-read in L2 (measured:
-  // 1.3-4 % faster for K = 3072-6144, within +-1 % at K = 8192-13824).
+  // 2-4.5 % faster for K = 3072-6144, within about 1 % either way at K = 8192-13824).
   p.stream_out = K <= kStreamOutMaxK ? 1 : 0;
   p.tiles_m = (int)((M + BM - 1) / BM);
   p.tiles_n = (int)((N + BN - 1) / BN);
