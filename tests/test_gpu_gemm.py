@@ -60,8 +60,10 @@ def test_w4a4_tiny_workload(gpu):
 
 
 @pytest.mark.parametrize("M,N,K", [(300, 520, 416), (513, 257, 1024), (64, 96, 96), (256, 256, 256),
-                                   (700, 384, 288), (1, 1, 32), (260, 300, 3072)])
+                                   (700, 384, 288), (1, 1, 32), (260, 300, 3072), (300, 520, 8704)])
 def test_w4a4_tiles_and_ragged_tails(gpu, M, N, K):
+    """K = 8704 takes the fast path with ordinary output stores (K above 8192); the other
+    whole-window shapes take it with non-temporal ones."""
     a = workloads.activations(M, K, "lognormal_channels", seed=M, name="ragged", device="cuda")
     w = workloads.weights(N, K, 0.02, seed=N, name="ragged", device="cuda")
     _w4a4_case(gpu, a, w, f"ragged{M}x{N}x{K}")
@@ -168,7 +170,7 @@ def _w4a8_case(mxq, a, w, label):
 
 
 _W4A8_TILES = [(300, 520, 1056), (513, 257, 1024), (260, 300, 5120), (700, 384, 5024), (256, 256, 3104),
-               (1, 1, 1024), (64, 96, 2080)]
+               (1, 1, 1024), (64, 96, 2080), (300, 520, 8704)]
 
 
 @pytest.mark.parametrize("dist", ["lognormal_channels", "student_t"])

@@ -40,7 +40,9 @@ LAYOUTS = [(8, 0), (4, 0), (1, 0), (8, 1)]
 
 
 @pytest.mark.parametrize("mode", ["w4a4", "w4a8", "bf16"])
-@pytest.mark.parametrize("K", [1024, 480])   # fast path; generic path (K % 64 != 0)
+# fast path with non-temporal staged stores (K <= 8192), with ordinary ones (K > 8192);
+# generic path (K % 64 != 0)
+@pytest.mark.parametrize("K", [1024, 8704, 480])
 def test_strided_outputs_match_contiguous(gpu, mode, K):
     run = _operands(gpu, mode, K)
     announce(f"epilogue {mode} {M}x{N}x{K} contiguous")
