@@ -65,11 +65,12 @@ def parse():
     p.add_argument("--workload", default=DEFAULT_WORKLOAD)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extras", action="store_true", help="time the step only (for profiling)")
+    p.add_argument("--no-configs", action="store_true", help="skip the other workloads' section")
     p.add_argument("--cpu-rows", type=int, default=2048, help="activation rows in the CPU oracle sample")
     p.add_argument("--config-reps", type=int, default=10, help="timed launches per kernel in the configs section")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for HBM counter scaling)")
-    p.add_argument("--summarize", choices=("trace", "pmc", "mfma"), help="summarize rocprofv3 CSV output")
+    p.add_argument("--summarize", choices=("trace", "pmc", "mfma", "stats"), help="summarize rocprofv3 CSV output")
     p.add_argument("--input", help="rocprofv3 output directory (--summarize; pmc: FETCH_DIR,WRITE_DIR)")
     p.add_argument("--copy-input", help="--copy-calibration counter directories COPY_FETCH_DIR,COPY_WRITE_DIR (pmc)")
     p.add_argument("--out", help="summary file to write (--summarize; pmc: a directory); stdout if absent")
@@ -479,7 +480,7 @@ def main_bench(args):
             extras(mxq, torch, st, res, dev)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(mxq, torch, st, min(args.cpu_rows, wl.M))
-    if not args.no_extras and args.workload == DEFAULT_WORKLOAD:
+    if not args.no_extras and not args.no_configs and args.workload == DEFAULT_WORKLOAD:
         del st
         torch.cuda.empty_cache()
         res["configs"] = configs_section(mxq, workloads, torch, dev, args.config_reps)
@@ -625,6 +626,24 @@ def summarize(args):
     elif args.summarize == "pmc":
         write_pmc_summaries(args, wl, steps)
         return
+    elif args.summarize == "stats":
+        # every library kernel of the run (step, MFMA ceilings and the follow-on rows), one
+        # line per kernel and launch grid (a grid stands for one shape), heaviest first
+        groups = {}
+        for r in _read_csvs(args.input, "kernel_trace.csv"):
+            name = _col(r, "Kernel_Name")
+            if not _is_mxq(name):
+                continue
+            key = (_short_name(name), int(_col(r, "Grid_Size_X")) // int(_col(r, "Workgroup_Size_X")))
+            groups.setdefault(key, []).append((int(_col(r, "End_Timestamp")) - int(_col(r, "Start_Timestamp"))) / 1e3)
+        lines.append(f"# Every library kernel of one bench.py run on workload {args.workload} "
+                     f"({wl.M}x{wl.K} @ {wl.K}x{wl.N}), MI355X (gfx950)")
+        lines.append(f"# command: {args.command}")
+        lines.append("# durations over all launches with that grid (warm-up launches included)")
+        lines.append(f"# {'calls':>6s} {'workgroups':>10s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s}   kernel")
+        for (kname, wgs), us in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            u = np.array(us)
+            lines.append(f"{len(u):8d} {wgs:10d} {u.mean():10.1f} {u.min():10.1f} {u.max():10.1f}   {kname}")
     else:
         by = _pmc_dispatches(args.input, wl, steps)
         if True:
