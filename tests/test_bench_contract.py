@@ -105,6 +105,21 @@ def test_trace_summary_matches_step_order(tmp_path):
     assert "command: rocprofv3" in text
 
 
+def test_stats_summary_groups_by_kernel_and_grid(tmp_path):
+    hdr = ["Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Workgroup_Size_X", "Grid_Size_X"]
+    q = "void mxq::(anonymous namespace)::mx_quantize_kernel<false, false, true>(void const*, long)"
+    rows = [[1, q, 0, 400000, 1024, 1024 * 16384], [2, q, 500000, 910000, 1024, 1024 * 16384],
+            [3, q, 1000000, 1034000, 1024, 1024 * 2160], [4, "at::native::copy", 0, 10, 256, 256]]
+    _write_csv(tmp_path / "prof" / "x_kernel_trace.csv", hdr, rows)
+    out = tmp_path / "stats.txt"
+    sys.argv = ["bench.py", "--summarize", "stats", "--input", str(tmp_path / "prof"), "--workload",
+                "wan_ffn_down_sqnr", "--out", str(out), "--command", "rocprofv3 --kernel-trace -- python bench.py"]
+    bench.main()
+    lines = [ln.split() for ln in out.read_text().splitlines() if not ln.startswith("#")]
+    assert [(ln[0], ln[1], ln[2]) for ln in lines] == [("2", "16384", "405.0"), ("1", "2160", "34.0")]
+    assert all("mx_quantize_kernel<false," in " ".join(ln) for ln in lines)   # torch's kernels left out
+
+
 def test_committed_summaries_name_their_kernel_and_command():
     prof = os.path.join(ROOT, "profiles")
     names = sorted(os.listdir(prof))
