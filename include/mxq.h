@@ -232,8 +232,9 @@ size_t mxq_gemm_w4a4_fused_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * 1e-5 * sum|a*b| + 1 bf16 ulp of the exact result except a few per million with heavy
  * cancellation, where one group of 8 holds E4M3 values ~2^14 apart.  Measured with
  * statically scaled activations drawn like the Wan2.2 FFN inputs (N(0,1) x LogNormal(0,1)
- * per channel; Student-t(3)), two seeds per case, 17.2M outputs each: 0 to 7 outside for
- * K = 2048 and 5120 (at most 1.91x the bound), 3 to 84 for K = 1024 (at most 2.85x); at
+ * per channel; Student-t(3)), up to eight seeds per case, 17.2M outputs each: 0 to 7
+ * outside for K = 2048 and 5120 (at most 1.91x the bound), 0 to 84 for K = 1024 (at most
+ * 2.85x); at
  * K = 288 / 416, 5 of ~425k (at most 1.31x).
  */
 mxq_status mxq_gemm_w4a8(const uint8_t* a_fp8, float a_scale,
