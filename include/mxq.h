@@ -234,8 +234,7 @@ size_t mxq_gemm_w4a4_fused_workspace_bytes(int64_t M, int64_t N, int64_t K);
  * statically scaled activations drawn like the Wan2.2 FFN inputs (N(0,1) x LogNormal(0,1)
  * per channel; Student-t(3)), up to eight seeds per case, 17.2M outputs each: 0 to 7
  * outside for K = 2048 and 5120 (at most 1.91x the bound), 0 to 84 for K = 1024 (at most
- * 2.85x); at
- * K = 288 / 416, 5 of ~425k (at most 1.31x).
+ * 2.85x); at K = 288 / 416, 5 of ~425k (at most 1.31x).
  */
 mxq_status mxq_gemm_w4a8(const uint8_t* a_fp8, float a_scale,
                          const uint8_t* w_codes, const uint8_t* w_scales,
