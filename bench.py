@@ -1,8 +1,8 @@
 """Benchmark of the MXFP4 hot path on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--no-extras]
-    python bench.py --summarize {trace,pmc,mfma} --input DIR --workload NAME [--out FILE]
+                    [--no-extras] [--no-configs]
+    python bench.py --summarize {trace,pmc,mfma,stats} --input DIR --workload NAME [--out FILE]
     python bench.py --copy-calibration
 
 A step is one pass of the whole hot path over one batch of synthetic activations already
@@ -26,14 +26,16 @@ workload, from its mean HIP-event time on the stream the kernels run on; `metric
 gives W4A4 and W4A8 beside each other; `roofline` is the W4A4 GEMM against the dense
 MXFP4 peak.  `kernels` gives every step kernel's rate (mean, median, standard deviation,
 coefficient of variation) against its own roofline.  Unless --no-extras: `configs` times
-the other workloads' own kernels the same way, `mfma_ceiling` the power-limited MFMA
+the other workloads' own kernels the same way (not with --no-configs), `mfma_ceiling` the
+power-limited MFMA
 ceiling on the step's operand bits, `next` the follow-on paths (fused W4A4, QDQ
 emulation, Hadamard rotation, UOS scales).  `cpu_baseline` times the CPU oracle on a
 bounded row sample of the same workload and checks its SQNR against the GPU's on the
 same rows.
 
 --summarize turns rocprofv3 CSV output (run on `bench.py --workload NAME --no-extras
---no-cpu-baseline`) into the text summaries kept under profiles/.
+--no-cpu-baseline`; for `stats`, a whole run with --no-configs) into the text summaries
+kept under profiles/.
 """
 
 import argparse
