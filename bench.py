@@ -27,9 +27,8 @@ gives W4A4 and W4A8 beside each other; `roofline` is the W4A4 GEMM against the d
 MXFP4 peak.  `kernels` gives every step kernel's rate (mean, median, standard deviation,
 coefficient of variation) against its own roofline.  Unless --no-extras: `configs` times
 the other workloads' own kernels the same way (not with --no-configs), `mfma_ceiling` the
-power-limited MFMA
-ceiling on the step's operand bits, `next` the follow-on paths (fused W4A4, QDQ
-emulation, Hadamard rotation, UOS scales).  `cpu_baseline` times the CPU oracle on a
+power-limited MFMA ceiling on the step's operand bits, `next` the follow-on paths (fused
+W4A4, QDQ emulation, Hadamard rotation, UOS scales).  `cpu_baseline` times the CPU oracle on a
 bounded row sample of the same workload and checks its SQNR against the GPU's on the
 same rows.
 
