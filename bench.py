@@ -71,7 +71,8 @@ def parse():
     p.add_argument("--config-reps", type=int, default=10, help="timed launches per kernel in the configs section")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run only a plain device copy of known size (for HBM counter scaling)")
-    p.add_argument("--summarize", choices=("trace", "pmc", "mfma", "stats"), help="summarize rocprofv3 CSV output")
+    p.add_argument("--summarize", choices=("trace", "pmc", "mfma", "stats", "waves"),
+                   help="summarize rocprofv3 CSV output")
     p.add_argument("--input", help="rocprofv3 output directory (--summarize; pmc: FETCH_DIR,WRITE_DIR)")
     p.add_argument("--copy-input", help="--copy-calibration counter directories COPY_FETCH_DIR,COPY_WRITE_DIR (pmc)")
     p.add_argument("--out", help="summary file to write (--summarize; pmc: a directory); stdout if absent")
@@ -627,6 +628,25 @@ def summarize(args):
     elif args.summarize == "pmc":
         write_pmc_summaries(args, wl, steps)
         return
+    elif args.summarize == "waves":
+        # where the step kernels' waves spend their time: SQ wave-cycle counters of one
+        # --pmc run, as fractions of the waves' lifetime (SQ_WAVE_CYCLES, the same units)
+        by = _pmc_dispatches(args.input, wl, steps)
+        lines.append(f"# Wave time breakdown per kernel, workload {args.workload}, MI355X (gfx950)")
+        lines.append(f"# command: {args.command}")
+        lines.append("# fractions of SQ_WAVE_CYCLES: wait = SQ_WAIT_ANY (s_waitcnt and barrier waits), "
+                     "issue_wait = SQ_WAIT_INST_ANY (waiting to issue), active = SQ_ACTIVE_INST_ANY, "
+                     "lds / vmem = SQ_ACTIVE_INST_LDS / _VMEM; lds_conflict = SQ_LDS_BANK_CONFLICT / "
+                     "SQ_LDS_IDX_ACTIVE")
+        for label, _ in step_kernels(wl):
+            evs = by[label][0::2] if label.startswith("mxq_sqnr") else by[label]
+            tot = lambda c: float(np.sum([e[2]["ctr"].get(c, 0.0) for e in evs]))
+            wc = max(tot("SQ_WAVE_CYCLES"), 1.0)
+            idx = max(tot("SQ_LDS_IDX_ACTIVE"), 1.0)
+            lines.append(f"{label:26s} launches {len(evs):3d} wait {tot('SQ_WAIT_ANY') / wc:.3f} "
+                         f"issue_wait {tot('SQ_WAIT_INST_ANY') / wc:.3f} active {tot('SQ_ACTIVE_INST_ANY') / wc:.3f} "
+                         f"lds {tot('SQ_ACTIVE_INST_LDS') / wc:.3f} vmem {tot('SQ_ACTIVE_INST_VMEM') / wc:.3f} "
+                         f"lds_conflict {tot('SQ_LDS_BANK_CONFLICT') / idx:.3f}")
     elif args.summarize == "stats":
         # every library kernel of the run (step, MFMA ceilings and the follow-on rows), one
         # line per kernel and launch grid (a grid stands for one shape), heaviest first
