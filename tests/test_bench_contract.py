@@ -120,6 +120,32 @@ def test_stats_summary_groups_by_kernel_and_grid(tmp_path):
     assert all("mx_quantize_kernel<false," in " ".join(ln) for ln in lines)   # torch's kernels left out
 
 
+def test_waves_summary_gives_fractions_of_wave_cycles(tmp_path):
+    import workloads
+    wl = workloads.WORKLOADS["flux_ffn_up_w4a4"]
+    seq = []
+    for label, n in bench.step_kernels(wl):
+        seq += [label] * n
+    names = {"mxq_quantize": "mx_quantize_kernel<false, false, true>", "mxq_gemm_w4a4": "gemm_fast_kernel<0, true>"}
+    ctr = {"SQ_WAVE_CYCLES": 1000.0, "SQ_WAIT_ANY": 150.0, "SQ_WAIT_INST_ANY": 450.0, "SQ_ACTIVE_INST_ANY": 400.0,
+           "SQ_ACTIVE_INST_LDS": 60.0, "SQ_ACTIVE_INST_VMEM": 40.0, "SQ_LDS_BANK_CONFLICT": 25.0,
+           "SQ_LDS_IDX_ACTIVE": 100.0}
+    rows, did = [], 0
+    for step in range(2):
+        for label in seq:
+            did += 1
+            for c, v in ctr.items():   # two shader engines' halves of each counter
+                rows += [[did, f"void mxq::(anonymous namespace)::{names[label]}(mxq::Params)", c, v / 2]] * 2
+    _write_csv(tmp_path / "prof" / "x_counter_collection.csv", ["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                                                "Counter_Value"], rows)
+    out = tmp_path / "waves.txt"
+    sys.argv = ["bench.py", "--summarize", "waves", "--input", str(tmp_path / "prof"), "--workload",
+                "flux_ffn_up_w4a4", "--out", str(out), "--command", "rocprofv3 --pmc ... -- python bench.py --steps 2"]
+    bench.main()
+    g = [ln for ln in out.read_text().splitlines() if ln.startswith("mxq_gemm_w4a4")][0]
+    assert "wait 0.150 issue_wait 0.450 active 0.400 lds 0.060 vmem 0.040 lds_conflict 0.250" in g
+
+
 def test_committed_summaries_name_their_kernel_and_command():
     prof = os.path.join(ROOT, "profiles")
     names = sorted(os.listdir(prof))
